@@ -1,0 +1,207 @@
+/*
+ * fp8lin.h - per-tensor dynamically scaled FP8 linear layer for MI355X (gfx950).
+ *
+ * C ABI of libfp8lin.so. Every entry point takes plain pointers and sizes and
+ * enqueues HIP kernels on the stream it is given. The library never allocates
+ * or frees memory, never synchronises the host with the device, never reads
+ * device memory from the host, and keeps no pointer after returning; the
+ * caller owns every buffer and must keep it alive until the stream work ends.
+ * All device-side scale data stays on the device, so a whole forward/backward
+ * step can be enqueued (or captured in a HIP graph) with no host round trip.
+ *
+ * The method (sources cited by page title and section):
+ *   [AMAX]  review of Perez, Zhang et al., "Training and inference of large
+ *           language models using 8-bit floating point", section "Proposed
+ *           method": per-tensor scaling biases from each tensor's max |x|
+ *           (bullet 1); compute_bias = log2(format max / amax) with a
+ *           configurable margin (bullet 2); scale before the FP8 cast and
+ *           undo the scaling after the matmul (bullet 3); E4 format for
+ *           weights and activations, E5 for gradients (bullet 4).
+ *   [FP8LM] reading note on Peng et al., "FP8-LM: Training FP8 Large
+ *           Language Models", section "Proposed method", O1, Eq. 3:
+ *           gradients are multiplied by an auto-scaling factor mu.
+ *
+ * Readings where the pages are silent: OCP E4M3FN (max 448, no inf) and
+ * E5M2 (max 57344); encode by round-to-nearest-even with saturation to
+ * +-max (inf included), NaN -> 0x7F|sign; bias = floor(log2(max/amax)) -
+ * margin + mu_log2 clamped to [-126, 126]; scale = 2^bias exactly; GEMM
+ * outputs are bf16, rounded to nearest even from the FP32 accumulator.
+ *
+ * Errors: every function checks its arguments before enqueuing anything and
+ * returns a status; it never aborts. Data-dependent conditions (a NaN in a
+ * tensor, a zero tensor, a clamped bias) are reported in fp8_scale_t.flags
+ * on the device, never as a status.
+ *
+ * Concurrency: calls that share an fp8_scale_t or an output buffer must be
+ * ordered on one stream (or by events); otherwise they race.
+ */
+#ifndef FP8LIN_H
+#define FP8LIN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FP8LIN_ABI_VERSION 1
+
+typedef enum fp8_fmt {
+  FP8_E4M3 = 0, /* OCP E4M3FN: weights and activations [AMAX bullet 4] */
+  FP8_E5M2 = 1  /* OCP E5M2: gradients [AMAX bullet 4] */
+} fp8_fmt;
+
+typedef enum fp8_status {
+  FP8_OK = 0,
+  FP8_ERR_INVALID = 1,     /* null / misaligned pointer, negative size, bad enum, out-of-range int */
+  FP8_ERR_UNSUPPORTED = 2, /* well-formed but outside what the kernels handle (e.g. a dim not a multiple of 16) */
+  FP8_ERR_HIP = 3          /* a HIP launch or runtime call failed */
+} fp8_status;
+
+/* flags in fp8_scale_t */
+#define FP8_FLAG_NONFINITE 1u /* the tensor holds a NaN or an inf: bias forced to 0 */
+#define FP8_FLAG_ZERO 2u      /* amax == 0: bias forced to 0 */
+#define FP8_FLAG_CLAMPED 4u   /* the bias rule left [-126, 126] and was clamped */
+
+/*
+ * Per-tensor scaling record. Lives in DEVICE memory, 32 bytes, 16-byte
+ * aligned. The public fields are written by fp8_amax / fp8_scale /
+ * fp8_amax_scale and read by fp8_cast and fp8_gemm_nt.
+ *   amax      max |t| over the tensor (a bf16 value widened to fp32); NaN if
+ *             the tensor holds a NaN, +inf if it holds an inf and no NaN.
+ *   bias      the integer exponent bias b [AMAX bullet 2].
+ *   scale     2^b: multiplies the tensor before the FP8 cast [AMAX bullet 3].
+ *   scale_inv 2^-b: undoes the scale after the GEMM.
+ *   flags     FP8_FLAG_* bits.
+ * The two reduce_* words are the amax reduction's working state. They must
+ * be zero before the first fp8_amax / fp8_amax_scale call on the record
+ * (allocate zeroed memory or call fp8_scale_reset once); every such call
+ * leaves them zero again when it completes.
+ */
+typedef struct fp8_scale_t {
+  float amax;
+  int32_t bias;
+  float scale;
+  float scale_inv;
+  uint32_t flags;
+  uint32_t reduce_bits;   /* internal: running max of the |bf16| bit patterns */
+  uint32_t reduce_ticket; /* internal: count of finished reduction blocks */
+  uint32_t reserved;
+} fp8_scale_t;
+
+/* Human-readable name of a status. Never NULL. */
+const char* fp8_status_str(fp8_status status);
+
+/* FP8LIN_ABI_VERSION of the built library. */
+int fp8_abi_version(void);
+
+/*
+ * Zero `count` scaling records (all fields) on `stream` with a kernel (no
+ * hipMemset, so it may be captured in a graph). s_dev: device, 16-B aligned.
+ */
+fp8_status fp8_scale_reset(fp8_scale_t* s_dev, int64_t count, hipStream_t stream);
+
+/*
+ * a1 - amax [AMAX bullet 1]: max |x| over n bf16 values, one pass over HBM.
+ *   x_bf16  device, n bf16 values, 16-B aligned (n may be 0: amax = 0).
+ *   s_dev   device record; writes amax and flags (NONFINITE / ZERO), sets
+ *           bias = 0, scale = scale_inv = 1 (call fp8_scale next).
+ */
+fp8_status fp8_amax(const void* x_bf16, int64_t n, fp8_scale_t* s_dev, hipStream_t stream);
+
+/*
+ * a2 - scale choice [AMAX bullet 2; FP8LM O1 Eq. 3], from s_dev->amax:
+ *   bias = clamp(floor(log2(fmt_max / amax)) - margin + mu_log2, -126, 126)
+ *   with fmt_max = 448 (E4M3) or 57344 (E5M2); amax = 0 or non-finite ->
+ *   bias 0 plus a flag. Writes bias, scale, scale_inv, flags.
+ *   margin, mu_log2: |value| <= 1024, else FP8_ERR_INVALID. mu = 2^mu_log2
+ *   is the gradient auto-scaling factor (pass 0 for weights/activations).
+ */
+fp8_status fp8_scale(fp8_fmt fmt, int margin, int mu_log2, fp8_scale_t* s_dev, hipStream_t stream);
+
+/* a1 + a2 in one kernel launch (the last reduction block picks the scale). */
+fp8_status fp8_amax_scale(const void* x_bf16, int64_t n, fp8_fmt fmt, int margin, int mu_log2,
+                          fp8_scale_t* s_dev, hipStream_t stream);
+
+/*
+ * The a2 rule on the host for one amax value (the same code the kernels
+ * run). Returns the bias; *flags_out (nullable) receives FP8_FLAG_* bits.
+ * Out-of-range margin/mu_log2 are clamped to +-1024.
+ */
+int32_t fp8_bias_host(float amax, fp8_fmt fmt, int margin, int mu_log2, uint32_t* flags_out);
+
+/*
+ * a3 - cast (+ transpose) [AMAX bullets 3-4]: q = enc_fmt(x * 2^bias) with
+ * round-to-nearest-even, saturation to +-max, subnormals kept, NaN ->
+ * 0x7F|sign; bias from s_dev (device).
+ *   x_bf16          device, [rows, cols] row-major bf16, 16-B aligned.
+ *   out_rowwise     device, [rows, cols] u8, or NULL to skip.
+ *   out_transposed  device, [cols, rows] u8, or NULL to skip.
+ *   rows, cols      >= 0 and multiples of 16 (else FP8_ERR_UNSUPPORTED).
+ */
+fp8_status fp8_cast(const void* x_bf16, int64_t rows, int64_t cols, fp8_fmt fmt,
+                    const fp8_scale_t* s_dev, uint8_t* out_rowwise, uint8_t* out_transposed,
+                    hipStream_t stream);
+
+/*
+ * a4-a6 - FP8 GEMM, NT form, FP32 accumulation on FP8 MFMA, dequantising
+ * bf16 epilogue [AMAX bullet 3]:
+ *   C[i, j] = bf16_rne( 2^-(sa.bias + sb.bias) * sum_r A[i, r] * B[j, r] )
+ *   A   device, [M, R] u8 codes of format fa, row-major (r contiguous).
+ *   B   device, [N, R] u8 codes of format fb, row-major (r contiguous).
+ *   C   device, [M, N] bf16 row-major (overwritten).
+ *   sa, sb  device scaling records of A and B.
+ *   M, N, R >= 0 and multiples of 16 (else FP8_ERR_UNSUPPORTED); R = 0 gives C = 0.
+ *   Forward:  Y  = gemm(A = x8 [M,K],  B = w8t [N,K])
+ *   Dgrad:    dX = gemm(A = dy8 [M,N], B = w8 [K,N])      (E5M2 x E4M3)
+ *   Wgrad:    dW = gemm(A = x8t [K,M], B = dy8t [N,M])    (E4M3 x E5M2)
+ * All pointers 16-B aligned.
+ */
+fp8_status fp8_gemm_nt(const uint8_t* A, fp8_fmt fa, const fp8_scale_t* sa, const uint8_t* B,
+                       fp8_fmt fb, const fp8_scale_t* sb, int64_t M, int64_t N, int64_t R,
+                       void* C_bf16, hipStream_t stream);
+
+/*
+ * Workspace of one FP8 linear: device pointers owned by the caller.
+ *   x8 [M,K], x8t [K,M], w8 [K,N], w8t [N,K], dy8 [M,N], dy8t [N,M]  (u8)
+ *   sx, sw, sdy: zero-initialised scaling records (see fp8_scale_t).
+ * The forward fills x8, x8t, w8, w8t, sx, sw; the backward reads them and
+ * fills dy8, dy8t, sdy.
+ */
+typedef struct fp8_linear_ws {
+  uint8_t* x8;
+  uint8_t* x8t;
+  uint8_t* w8;
+  uint8_t* w8t;
+  uint8_t* dy8;
+  uint8_t* dy8t;
+  fp8_scale_t* sx;
+  fp8_scale_t* sw;
+  fp8_scale_t* sdy;
+} fp8_linear_ws;
+
+/*
+ * Forward of one linear, Y = X W: amax+scale of X and W (E4M3), cast
+ * (+transpose) of both, then the forward GEMM.
+ *   X [M,K] bf16, W [K,N] bf16 (in x out), Y [M,N] bf16; device, 16-B aligned.
+ *   M, K, N multiples of 16. ws: host struct of device pointers (above).
+ */
+fp8_status fp8_linear_fwd(const void* X, const void* W, int64_t M, int64_t K, int64_t N, int margin,
+                          const fp8_linear_ws* ws, void* Y, hipStream_t stream);
+
+/*
+ * Backward of one linear: amax+scale of dY (E5M2, with mu = 2^mu_log2),
+ * cast (+transpose) of dY, then dX = dY W^T and dW = X^T dY from the FP8
+ * copies the forward left in ws.
+ *   dY [M,N] bf16; dX [M,K] bf16 or NULL to skip; dW [K,N] bf16 or NULL to skip.
+ */
+fp8_status fp8_linear_bwd(const void* dY, int64_t M, int64_t K, int64_t N, int margin, int mu_log2,
+                          const fp8_linear_ws* ws, void* dX, void* dW, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8LIN_H */

@@ -1,0 +1,209 @@
+"""Thin Python binding over the C ABI (include/fp8lin.h): argument
+marshalling only. Torch supplies device memory and the current HIP stream;
+every step of the computation runs in the HIP kernels of libfp8lin.so.
+
+Names follow the C entry points: fp8_amax, fp8_scale, fp8_amax_scale,
+fp8_cast, fp8_gemm_nt, fp8_linear_fwd, fp8_linear_bwd. A scaling record
+(fp8_scale_t, 32 bytes) is an int32 tensor of 8 words on the device."""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+import torch
+
+from . import _lib
+from ._lib import FP8_E4M3, FP8_E5M2, LinearWs, check, load
+
+SCALE_WORDS = 8          # sizeof(fp8_scale_t) / 4
+FMT_CODES = {"e4m3": FP8_E4M3, "e5m2": FP8_E5M2, FP8_E4M3: FP8_E4M3, FP8_E5M2: FP8_E5M2}
+
+
+def _fmt(f) -> int:
+    try:
+        return FMT_CODES[f]
+    except KeyError:
+        raise ValueError(f"unknown FP8 format {f!r}") from None
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _dev(t: Optional[torch.Tensor], dtype, name: str) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor (no CPU path exists)")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def new_scale(count: int = 1, device="cuda") -> torch.Tensor:
+    """Zeroed scaling record(s): int32 [count, 8] (or [8] for count=1 via [0])."""
+    return torch.zeros((count, SCALE_WORDS), dtype=torch.int32, device=device)
+
+
+def read_scale(s: torch.Tensor) -> dict:
+    """Copy a record to the host (synchronises) and decode its fields."""
+    w = s.reshape(-1, SCALE_WORDS)[0].cpu()
+    f = w.view(torch.float32)
+    return {"amax": float(f[0]), "bias": int(w[1]), "scale": float(f[2]),
+            "scale_inv": float(f[3]), "flags": int(w[4]) & 0xFFFFFFFF,
+            "reduce_bits": int(w[5]) & 0xFFFFFFFF, "reduce_ticket": int(w[6]) & 0xFFFFFFFF}
+
+
+def fp8_scale_reset(s: torch.Tensor) -> None:
+    n = s.numel() // SCALE_WORDS
+    check(load().fp8_scale_reset(_dev(s, torch.int32, "s"), n, _stream(s)), "fp8_scale_reset")
+
+
+def fp8_amax(x: torch.Tensor, s: torch.Tensor) -> None:
+    check(load().fp8_amax(_dev(x, torch.bfloat16, "x"), x.numel(), _dev(s, torch.int32, "s"),
+                          _stream(x)), "fp8_amax")
+
+
+def fp8_scale(fmt, s: torch.Tensor, margin: int = 0, mu_log2: int = 0) -> None:
+    check(load().fp8_scale(_fmt(fmt), margin, mu_log2, _dev(s, torch.int32, "s"), _stream(s)),
+          "fp8_scale")
+
+
+def fp8_amax_scale(x: torch.Tensor, fmt, s: torch.Tensor, margin: int = 0, mu_log2: int = 0) -> None:
+    check(load().fp8_amax_scale(_dev(x, torch.bfloat16, "x"), x.numel(), _fmt(fmt), margin, mu_log2,
+                                _dev(s, torch.int32, "s"), _stream(x)), "fp8_amax_scale")
+
+
+def fp8_bias_host(amax: float, fmt, margin: int = 0, mu_log2: int = 0):
+    flags = ctypes.c_uint32(0)
+    b = load().fp8_bias_host(float(amax), _fmt(fmt), margin, mu_log2, ctypes.byref(flags))
+    return int(b), int(flags.value)
+
+
+def fp8_cast(x: torch.Tensor, fmt, s: torch.Tensor, out_row: Optional[torch.Tensor] = None,
+             out_t: Optional[torch.Tensor] = None, rowwise: bool = True, transposed: bool = True):
+    """Cast a bf16 [rows, cols] matrix; returns (rowwise [rows, cols] u8 or None,
+    transposed [cols, rows] u8 or None)."""
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D")
+    rows, cols = x.shape
+    if rowwise and out_row is None:
+        out_row = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    if transposed and out_t is None:
+        out_t = torch.empty((cols, rows), dtype=torch.uint8, device=x.device)
+    check(load().fp8_cast(_dev(x, torch.bfloat16, "x"), rows, cols, _fmt(fmt), _dev(s, torch.int32, "s"),
+                          _dev(out_row, torch.uint8, "out_row"), _dev(out_t, torch.uint8, "out_t"),
+                          _stream(x)), "fp8_cast")
+    return out_row, out_t
+
+
+def fp8_gemm_nt(a: torch.Tensor, fa, sa: torch.Tensor, b: torch.Tensor, fb, sb: torch.Tensor,
+                out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """C[M, N] (bf16) = 2^-(bias_a + bias_b) * A[M, R] . B[N, R]^T on FP8 codes."""
+    if a.dim() != 2 or b.dim() != 2 or a.shape[1] != b.shape[1]:
+        raise ValueError(f"shape mismatch: A {tuple(a.shape)}, B {tuple(b.shape)}")
+    M, R = a.shape
+    N = b.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    if tuple(out.shape) != (M, N):
+        raise ValueError("out has the wrong shape")
+    check(load().fp8_gemm_nt(_dev(a, torch.uint8, "A"), _fmt(fa), _dev(sa, torch.int32, "sa"),
+                             _dev(b, torch.uint8, "B"), _fmt(fb), _dev(sb, torch.int32, "sb"),
+                             M, N, R, _dev(out, torch.bfloat16, "out"), _stream(a)), "fp8_gemm_nt")
+    return out
+
+
+class LinearWorkspace:
+    """Device buffers of one FP8 linear (FP8 copies of X, W, dY in both
+    layouts and the three scaling records)."""
+
+    def __init__(self, M: int, K: int, N: int, device="cuda"):
+        u8 = dict(dtype=torch.uint8, device=device)
+        self.M, self.K, self.N = M, K, N
+        self.x8 = torch.empty((M, K), **u8)
+        self.x8t = torch.empty((K, M), **u8)
+        self.w8 = torch.empty((K, N), **u8)
+        self.w8t = torch.empty((N, K), **u8)
+        self.dy8 = torch.empty((M, N), **u8)
+        self.dy8t = torch.empty((N, M), **u8)
+        self.scales = new_scale(3, device)
+        self.sx, self.sw, self.sdy = self.scales[0], self.scales[1], self.scales[2]
+        self.c = LinearWs(*[t.data_ptr() for t in (self.x8, self.x8t, self.w8, self.w8t, self.dy8,
+                                                    self.dy8t, self.sx, self.sw, self.sdy)])
+
+
+def fp8_linear_fwd(X: torch.Tensor, W: torch.Tensor, ws: LinearWorkspace, margin: int = 0,
+                   Y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    M, K = X.shape
+    K2, N = W.shape
+    if K2 != K or (ws.M, ws.K, ws.N) != (M, K, N):
+        raise ValueError("shape mismatch between X, W and the workspace")
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device=X.device)
+    check(load().fp8_linear_fwd(_dev(X, torch.bfloat16, "X"), _dev(W, torch.bfloat16, "W"), M, K, N,
+                                margin, ctypes.byref(ws.c), _dev(Y, torch.bfloat16, "Y"), _stream(X)),
+          "fp8_linear_fwd")
+    return Y
+
+
+def fp8_linear_bwd(dY: torch.Tensor, ws: LinearWorkspace, margin: int = 0, mu_log2: int = 0,
+                   dX: Optional[torch.Tensor] = None, dW: Optional[torch.Tensor] = None,
+                   need_dx: bool = True, need_dw: bool = True):
+    M, K, N = ws.M, ws.K, ws.N
+    if tuple(dY.shape) != (M, N):
+        raise ValueError("dY has the wrong shape")
+    if need_dx and dX is None:
+        dX = torch.empty((M, K), dtype=torch.bfloat16, device=dY.device)
+    if need_dw and dW is None:
+        dW = torch.empty((K, N), dtype=torch.bfloat16, device=dY.device)
+    check(load().fp8_linear_bwd(_dev(dY, torch.bfloat16, "dY"), M, K, N, margin, mu_log2,
+                                ctypes.byref(ws.c), _dev(dX, torch.bfloat16, "dX"),
+                                _dev(dW, torch.bfloat16, "dW"), _stream(dY)), "fp8_linear_bwd")
+    return dX, dW
+
+
+class _FP8LinearFn(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, X, W, margin, mu_log2):
+        Xc, Wc = X.contiguous(), W.contiguous()
+        lead = Xc.shape[:-1]
+        X2 = Xc.reshape(-1, Xc.shape[-1])
+        ws = LinearWorkspace(X2.shape[0], X2.shape[1], Wc.shape[1], X.device)
+        Y = fp8_linear_fwd(X2, Wc, ws, margin)
+        ctx.ws, ctx.margin, ctx.mu_log2, ctx.lead = ws, margin, mu_log2, lead
+        return Y.reshape(*lead, Wc.shape[1])
+
+    @staticmethod
+    def backward(ctx, dY):
+        dY2 = dY.contiguous().reshape(-1, dY.shape[-1])
+        if dY2.dtype != torch.bfloat16:
+            dY2 = dY2.to(torch.bfloat16)
+        dX, dW = fp8_linear_bwd(dY2, ctx.ws, ctx.margin, ctx.mu_log2,
+                                need_dx=ctx.needs_input_grad[0], need_dw=ctx.needs_input_grad[1])
+        if dX is not None:
+            dX = dX.reshape(*ctx.lead, dX.shape[-1])
+        return dX, dW, None, None
+
+
+def linear(X: torch.Tensor, W: torch.Tensor, margin: int = 0, mu_log2: int = 0) -> torch.Tensor:
+    """Y = X W with per-tensor dynamically scaled FP8 (E4M3 X and W, E5M2 dY).
+    X [..., K] bf16, W [K, N] bf16 (in x out)."""
+    return _FP8LinearFn.apply(X, W, margin, mu_log2)
+
+
+class Linear(torch.nn.Module):
+    """Drop-in FP8 linear layer (no bias term); weight stored [in, out] in bf16."""
+
+    def __init__(self, in_features: int, out_features: int, margin: int = 0, mu_log2: int = 0,
+                 device=None):
+        super().__init__()
+        self.weight = torch.nn.Parameter(
+            torch.empty((in_features, out_features), dtype=torch.bfloat16, device=device))
+        torch.nn.init.normal_(self.weight, std=0.02)
+        self.margin, self.mu_log2 = margin, mu_log2
+
+    def forward(self, x):
+        return linear(x, self.weight, self.margin, self.mu_log2)

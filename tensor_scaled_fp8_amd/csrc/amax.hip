@@ -1,0 +1,152 @@
+// a1 amax (+ fused a2 scale choice) over a bf16 tensor.
+//
+// [Perez et al. review, "Proposed method", bullets 1-2] the scaling bias of
+// a tensor comes from its max |x|. One pass over HBM with 16-byte loads.
+// |x| is compared on the 15-bit magnitude pattern: for bf16, integer order
+// of (bits & 0x7FFF) is the order of |x|, with inf above every finite value
+// and NaN patterns above inf, so the integer max also detects non-finite
+// values. Two packed 16-bit maxima per dword (one VALU op per two values),
+// a wavefront max by cross-lane exchange, a block max through LDS, then one
+// device-scope atomic max per block. The block that finishes last (ticket
+// counter) publishes amax and, when fused, the scale; it leaves the
+// reduction words at zero for the next call.
+#include "fp8lin_internal.h"
+
+namespace fp8lin {
+namespace {
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 8;         // 16-byte loads in flight per thread
+constexpr int kMaxBlocks = 2048;   // 8 blocks per CU on 256 CUs
+
+__device__ inline u16x2 as_u16x2(uint32_t v) { return __builtin_bit_cast(u16x2, v); }
+__device__ inline uint32_t as_u32(u16x2 v) { return __builtin_bit_cast(uint32_t, v); }
+
+__device__ inline u16x2 vmax(u16x2 a, uint32_t w) {
+  return __builtin_elementwise_max(a, as_u16x2(w & 0x7FFF7FFFu));
+}
+
+__device__ inline void write_scale(fp8_scale_t* s, uint32_t mag, bool fuse, int fmt, int margin,
+                                   int mu_log2) {
+  union { uint32_t u; float f; } a;
+  a.u = mag << 16;
+  uint32_t flags = 0;
+  int32_t b = 0;
+  if (fuse) {
+    b = bias_from_amax_bits(mag << 16, fmt, margin, mu_log2, &flags);
+  } else {
+    flags = mag >= 0x7F80u ? FP8_FLAG_NONFINITE : (mag == 0u ? FP8_FLAG_ZERO : 0u);
+  }
+  s->amax = a.f;
+  s->bias = b;
+  s->scale = pow2f(b);
+  s->scale_inv = pow2f(-b);
+  s->flags = flags;
+}
+
+__global__ __launch_bounds__(kThreads) void amax_kernel(const uint4* __restrict__ x, int64_t n_vec,
+                                                        const uint16_t* __restrict__ tail,
+                                                        int tail_n, fp8_scale_t* s, int fuse,
+                                                        int fmt, int margin, int mu_log2) {
+  u16x2 m = {0, 0};
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  // main sweep: kUnroll independent loads per iteration
+  for (; i + (kUnroll - 1) * stride < n_vec; i += kUnroll * stride) {
+    uint4 v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) v[u] = x[i + u * stride];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      m = vmax(m, v[u].x);
+      m = vmax(m, v[u].y);
+      m = vmax(m, v[u].z);
+      m = vmax(m, v[u].w);
+    }
+  }
+  for (; i < n_vec; i += stride) {
+    uint4 v = x[i];
+    m = vmax(m, v.x);
+    m = vmax(m, v.y);
+    m = vmax(m, v.z);
+    m = vmax(m, v.w);
+  }
+  if (blockIdx.x == 0 && (int)threadIdx.x < tail_n) {
+    m = vmax(m, (uint32_t)tail[threadIdx.x]);
+  }
+  uint32_t r = m.x > m.y ? m.x : m.y;
+  // wavefront max
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    uint32_t o = (uint32_t)__shfl_xor((int)r, off, 64);
+    r = o > r ? o : r;
+  }
+  __shared__ uint32_t wmax[kThreads / 64];
+  __shared__ int last;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  if (lane == 0) wmax[wid] = r;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t b = wmax[0];
+#pragma unroll
+    for (int w = 1; w < kThreads / 64; ++w) b = wmax[w] > b ? wmax[w] : b;
+    if (b != 0u) atomicMax(&s->reduce_bits, b);
+    __threadfence();
+    const uint32_t t = atomicAdd(&s->reduce_ticket, 1u);
+    last = (t == gridDim.x - 1);
+  }
+  __syncthreads();
+  if (last && threadIdx.x == 0) {
+    __threadfence();
+    const uint32_t mag = atomicExch(&s->reduce_bits, 0u);
+    atomicExch(&s->reduce_ticket, 0u);
+    write_scale(s, mag, fuse != 0, fmt, margin, mu_log2);
+  }
+}
+
+__global__ void scale_kernel(fp8_scale_t* s, int fmt, int margin, int mu_log2) {
+  union { float f; uint32_t u; } a;
+  a.f = s->amax;
+  uint32_t flags;
+  int32_t b = bias_from_amax_bits(a.u & 0x7FFFFFFFu, fmt, margin, mu_log2, &flags);
+  s->bias = b;
+  s->scale = pow2f(b);
+  s->scale_inv = pow2f(-b);
+  s->flags = flags;
+}
+
+__global__ void scale_reset_kernel(uint4* s, int64_t n16) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n16) s[i] = make_uint4(0, 0, 0, 0);
+}
+
+}  // namespace
+
+hipError_t launch_scale_reset(fp8_scale_t* s, int64_t count, hipStream_t st) {
+  if (count == 0) return hipSuccess;
+  const int64_t n16 = count * (int64_t)(sizeof(fp8_scale_t) / 16);
+  const int64_t blocks = (n16 + 255) / 256;
+  hipLaunchKernelGGL(scale_reset_kernel, dim3((unsigned)blocks), dim3(256), 0, st, (uint4*)s, n16);
+  return hipGetLastError();
+}
+
+hipError_t launch_amax(const void* x, int64_t n, fp8_scale_t* s, bool fuse_scale, int fmt, int margin,
+                       int mu_log2, hipStream_t st) {
+  const int64_t n_vec = n / 8;
+  const int tail_n = (int)(n - n_vec * 8);
+  const uint16_t* tail = (const uint16_t*)x + n_vec * 8;
+  int64_t want = (n_vec + (int64_t)kThreads * kUnroll - 1) / ((int64_t)kThreads * kUnroll);
+  int blocks = (int)(want < 1 ? 1 : (want > kMaxBlocks ? kMaxBlocks : want));
+  hipLaunchKernelGGL(amax_kernel, dim3(blocks), dim3(kThreads), 0, st, (const uint4*)x, n_vec, tail,
+                     tail_n, s, fuse_scale ? 1 : 0, fmt, margin, mu_log2);
+  return hipGetLastError();
+}
+
+hipError_t launch_scale(fp8_scale_t* s, int fmt, int margin, int mu_log2, hipStream_t st) {
+  hipLaunchKernelGGL(scale_kernel, dim3(1), dim3(1), 0, st, s, fmt, margin, mu_log2);
+  return hipGetLastError();
+}
+
+}  // namespace fp8lin

@@ -1,0 +1,149 @@
+// C-ABI entry points of libfp8lin.so: argument validation, then kernel
+// launches on the caller's stream. No allocation, no host synchronisation.
+#include <string.h>
+
+#include "fp8lin_internal.h"
+
+using namespace fp8lin;
+
+namespace {
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+inline bool fmt_ok(int f) { return f == FP8_E4M3 || f == FP8_E5M2; }
+inline bool int_ok(int v) { return v >= -kIntArgLimit && v <= kIntArgLimit; }
+constexpr int64_t kMaxDim = (int64_t)1 << 31;  // per-dimension limit (tile indices are 32-bit)
+inline fp8_status hip_status(hipError_t e) { return e == hipSuccess ? FP8_OK : FP8_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* fp8_status_str(fp8_status s) {
+  switch (s) {
+    case FP8_OK: return "ok";
+    case FP8_ERR_INVALID: return "invalid argument";
+    case FP8_ERR_UNSUPPORTED: return "unsupported shape or format";
+    case FP8_ERR_HIP: return "HIP launch or runtime error";
+  }
+  return "unknown status";
+}
+
+int fp8_abi_version(void) { return FP8LIN_ABI_VERSION; }
+
+fp8_status fp8_scale_reset(fp8_scale_t* s_dev, int64_t count, hipStream_t stream) {
+  if (count < 0 || (count > 0 && (!s_dev || !aligned16(s_dev)))) return FP8_ERR_INVALID;
+  return hip_status(launch_scale_reset(s_dev, count, stream));
+}
+
+fp8_status fp8_amax(const void* x_bf16, int64_t n, fp8_scale_t* s_dev, hipStream_t stream) {
+  if (n < 0 || !s_dev || !aligned16(s_dev)) return FP8_ERR_INVALID;
+  if (n > 0 && (!x_bf16 || !aligned16(x_bf16))) return FP8_ERR_INVALID;
+  return hip_status(launch_amax(x_bf16, n, s_dev, false, 0, 0, 0, stream));
+}
+
+fp8_status fp8_scale(fp8_fmt fmt, int margin, int mu_log2, fp8_scale_t* s_dev, hipStream_t stream) {
+  if (!fmt_ok(fmt) || !int_ok(margin) || !int_ok(mu_log2) || !s_dev || !aligned16(s_dev))
+    return FP8_ERR_INVALID;
+  return hip_status(launch_scale(s_dev, fmt, margin, mu_log2, stream));
+}
+
+fp8_status fp8_amax_scale(const void* x_bf16, int64_t n, fp8_fmt fmt, int margin, int mu_log2,
+                          fp8_scale_t* s_dev, hipStream_t stream) {
+  if (n < 0 || !fmt_ok(fmt) || !int_ok(margin) || !int_ok(mu_log2) || !s_dev || !aligned16(s_dev))
+    return FP8_ERR_INVALID;
+  if (n > 0 && (!x_bf16 || !aligned16(x_bf16))) return FP8_ERR_INVALID;
+  return hip_status(launch_amax(x_bf16, n, s_dev, true, fmt, margin, mu_log2, stream));
+}
+
+int32_t fp8_bias_host(float amax, fp8_fmt fmt, int margin, int mu_log2, uint32_t* flags_out) {
+  uint32_t bits;
+  memcpy(&bits, &amax, 4);
+  if (margin > kIntArgLimit) margin = kIntArgLimit;
+  if (margin < -kIntArgLimit) margin = -kIntArgLimit;
+  if (mu_log2 > kIntArgLimit) mu_log2 = kIntArgLimit;
+  if (mu_log2 < -kIntArgLimit) mu_log2 = -kIntArgLimit;
+  return bias_from_amax_bits(bits & 0x7FFFFFFFu, fmt, margin, mu_log2, flags_out);
+}
+
+fp8_status fp8_cast(const void* x_bf16, int64_t rows, int64_t cols, fp8_fmt fmt,
+                    const fp8_scale_t* s_dev, uint8_t* out_rowwise, uint8_t* out_transposed,
+                    hipStream_t stream) {
+  if (rows < 0 || cols < 0 || !fmt_ok(fmt) || !s_dev || !aligned16(s_dev)) return FP8_ERR_INVALID;
+  if (rows % 16 || cols % 16 || rows >= kMaxDim || cols >= kMaxDim) return FP8_ERR_UNSUPPORTED;
+  if (rows > 0 && cols > 0) {
+    if (!x_bf16 || !aligned16(x_bf16)) return FP8_ERR_INVALID;
+    if (out_rowwise && !aligned16(out_rowwise)) return FP8_ERR_INVALID;
+    if (out_transposed && !aligned16(out_transposed)) return FP8_ERR_INVALID;
+  }
+  return hip_status(launch_cast(x_bf16, rows, cols, fmt, s_dev, out_rowwise, out_transposed, stream));
+}
+
+fp8_status fp8_gemm_nt(const uint8_t* A, fp8_fmt fa, const fp8_scale_t* sa, const uint8_t* B,
+                       fp8_fmt fb, const fp8_scale_t* sb, int64_t M, int64_t N, int64_t R,
+                       void* C_bf16, hipStream_t stream) {
+  if (M < 0 || N < 0 || R < 0 || !fmt_ok(fa) || !fmt_ok(fb)) return FP8_ERR_INVALID;
+  if (!sa || !sb || !aligned16(sa) || !aligned16(sb)) return FP8_ERR_INVALID;
+  if (M % 16 || N % 16 || R % 16 || M >= kMaxDim || N >= kMaxDim || R >= kMaxDim)
+    return FP8_ERR_UNSUPPORTED;
+  if (M > 0 && N > 0) {
+    if (!C_bf16 || !aligned16(C_bf16)) return FP8_ERR_INVALID;
+    if (R > 0 && (!A || !B || !aligned16(A) || !aligned16(B))) return FP8_ERR_INVALID;
+  }
+  return hip_status(launch_gemm(A, fa, sa, B, fb, sb, M, N, R, C_bf16, stream));
+}
+
+static fp8_status check_ws(const fp8_linear_ws* ws, bool fwd) {
+  if (!ws) return FP8_ERR_INVALID;
+  const void* p[] = {ws->x8, ws->x8t, ws->w8, ws->w8t, ws->sx, ws->sw};
+  for (const void* q : p)
+    if (!q || !aligned16(q)) return FP8_ERR_INVALID;
+  if (!fwd) {
+    const void* r[] = {ws->dy8, ws->dy8t, ws->sdy};
+    for (const void* q : r)
+      if (!q || !aligned16(q)) return FP8_ERR_INVALID;
+  }
+  return FP8_OK;
+}
+
+fp8_status fp8_linear_fwd(const void* X, const void* W, int64_t M, int64_t K, int64_t N, int margin,
+                          const fp8_linear_ws* ws, void* Y, hipStream_t stream) {
+  if (M < 0 || K < 0 || N < 0 || !int_ok(margin)) return FP8_ERR_INVALID;
+  if (M % 16 || K % 16 || N % 16 || M >= kMaxDim || K >= kMaxDim || N >= kMaxDim)
+    return FP8_ERR_UNSUPPORTED;
+  fp8_status st = check_ws(ws, true);
+  if (st != FP8_OK) return st;
+  if ((M * K > 0 && (!X || !aligned16(X))) || (K * N > 0 && (!W || !aligned16(W))) ||
+      (M * N > 0 && (!Y || !aligned16(Y))))
+    return FP8_ERR_INVALID;
+  hipError_t e;
+  if ((e = launch_amax(X, M * K, ws->sx, true, FP8_E4M3, margin, 0, stream)) != hipSuccess) return FP8_ERR_HIP;
+  if ((e = launch_amax(W, K * N, ws->sw, true, FP8_E4M3, margin, 0, stream)) != hipSuccess) return FP8_ERR_HIP;
+  if ((e = launch_cast(X, M, K, FP8_E4M3, ws->sx, ws->x8, ws->x8t, stream)) != hipSuccess) return FP8_ERR_HIP;
+  if ((e = launch_cast(W, K, N, FP8_E4M3, ws->sw, ws->w8, ws->w8t, stream)) != hipSuccess) return FP8_ERR_HIP;
+  return hip_status(launch_gemm(ws->x8, FP8_E4M3, ws->sx, ws->w8t, FP8_E4M3, ws->sw, M, N, K, Y, stream));
+}
+
+fp8_status fp8_linear_bwd(const void* dY, int64_t M, int64_t K, int64_t N, int margin, int mu_log2,
+                          const fp8_linear_ws* ws, void* dX, void* dW, hipStream_t stream) {
+  if (M < 0 || K < 0 || N < 0 || !int_ok(margin) || !int_ok(mu_log2)) return FP8_ERR_INVALID;
+  if (M % 16 || K % 16 || N % 16 || M >= kMaxDim || K >= kMaxDim || N >= kMaxDim)
+    return FP8_ERR_UNSUPPORTED;
+  fp8_status st = check_ws(ws, false);
+  if (st != FP8_OK) return st;
+  if ((M * N > 0 && (!dY || !aligned16(dY))) || (dX && !aligned16(dX)) || (dW && !aligned16(dW)))
+    return FP8_ERR_INVALID;
+  hipError_t e;
+  if ((e = launch_amax(dY, M * N, ws->sdy, true, FP8_E5M2, margin, mu_log2, stream)) != hipSuccess)
+    return FP8_ERR_HIP;
+  if ((e = launch_cast(dY, M, N, FP8_E5M2, ws->sdy, ws->dy8, ws->dy8t, stream)) != hipSuccess)
+    return FP8_ERR_HIP;
+  if (dX && (e = launch_gemm(ws->dy8, FP8_E5M2, ws->sdy, ws->w8, FP8_E4M3, ws->sw, M, K, N, dX, stream)) !=
+                hipSuccess)
+    return FP8_ERR_HIP;
+  if (dW && (e = launch_gemm(ws->x8t, FP8_E4M3, ws->sx, ws->dy8t, FP8_E5M2, ws->sdy, K, N, M, dW, stream)) !=
+                hipSuccess)
+    return FP8_ERR_HIP;
+  return FP8_OK;
+}
+
+}  // extern "C"

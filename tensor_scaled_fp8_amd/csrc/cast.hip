@@ -1,0 +1,162 @@
+// a3 cast (+ transpose): bf16 [rows, cols] -> FP8 codes, row-wise [rows, cols]
+// and transposed [cols, rows].
+//
+// [Perez et al. review, "Proposed method", bullets 3-4] the tensor is
+// multiplied by its scale 2^bias before the FP8 cast (E4M3 for weights and
+// activations, E5M2 for gradients). The product is exact (a power of two);
+// it is clamped to +-max (saturation; inf -> max) and converted by the
+// hardware FP8 converter, which rounds to nearest even and keeps
+// subnormals. NaN inputs (only possible when the tensor's record carries
+// FP8_FLAG_NONFINITE) are patched to 0x7F|sign afterwards.
+//
+// Tiling: one 256-thread block per 128 x 128 tile. Each thread loads an
+// 8 x 8 patch (eight 16-byte row loads), converts it, stores its eight
+// 8-byte row-wise pieces, transposes the 8 x 8 bytes in registers
+// (byte permutes) and writes eight 8-byte column pieces into an LDS tile
+// laid out transposed. After a barrier the block streams the transposed
+// tile out as 16-byte stores, 128 contiguous bytes per output row, so both
+// outputs are written in whole 128-byte lines. LDS chunks are XOR-swizzled
+// by (row / 8) so the 8-byte column writes spread over the banks.
+#include "fp8lin_internal.h"
+
+namespace fp8lin {
+namespace {
+
+constexpr int kTile = 128;
+constexpr int kThreads = 256;
+
+template <int FMT>
+__device__ inline uint32_t cvt4(uint32_t w0, uint32_t w1, float scale) {
+  constexpr float kMax = FMT == FP8_E4M3 ? 448.0f : 57344.0f;
+  float f0 = __uint_as_float(w0 << 16) * scale;
+  float f1 = __uint_as_float(w0 & 0xFFFF0000u) * scale;
+  float f2 = __uint_as_float(w1 << 16) * scale;
+  float f3 = __uint_as_float(w1 & 0xFFFF0000u) * scale;
+  f0 = fminf(fmaxf(f0, -kMax), kMax);
+  f1 = fminf(fmaxf(f1, -kMax), kMax);
+  f2 = fminf(fmaxf(f2, -kMax), kMax);
+  f3 = fminf(fmaxf(f3, -kMax), kMax);
+  int r;
+  if constexpr (FMT == FP8_E4M3) {
+    r = __builtin_amdgcn_cvt_pk_fp8_f32(f0, f1, 0, false);
+    r = __builtin_amdgcn_cvt_pk_fp8_f32(f2, f3, r, true);
+  } else {
+    r = __builtin_amdgcn_cvt_pk_bf8_f32(f0, f1, 0, false);
+    r = __builtin_amdgcn_cvt_pk_bf8_f32(f2, f3, r, true);
+  }
+  return (uint32_t)r;
+}
+
+// NaN bf16 inputs -> 0x7F with the input's sign, byte by byte.
+__device__ inline uint32_t patch_nan(uint32_t q, uint32_t w0, uint32_t w1) {
+  const uint32_t h[4] = {w0 & 0xFFFFu, w0 >> 16, w1 & 0xFFFFu, w1 >> 16};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    if ((h[k] & 0x7FFFu) > 0x7F80u) {
+      const uint32_t code = 0x7Fu | ((h[k] >> 8) & 0x80u);
+      q = (q & ~(0xFFu << (8 * k))) | (code << (8 * k));
+    }
+  }
+  return q;
+}
+
+// 4 x 4 byte transpose: in[i] holds row i (bytes = cols 0..3); out[j] holds
+// column j (bytes = rows 0..3).
+__device__ inline void transpose4(const uint32_t in[4], uint32_t out[4]) {
+  const uint32_t a0 = __builtin_amdgcn_perm(in[1], in[0], 0x05010400u);  // r0c0 r1c0 r0c1 r1c1
+  const uint32_t a1 = __builtin_amdgcn_perm(in[1], in[0], 0x07030602u);  // r0c2 r1c2 r0c3 r1c3
+  const uint32_t b0 = __builtin_amdgcn_perm(in[3], in[2], 0x05010400u);  // r2c0 r3c0 r2c1 r3c1
+  const uint32_t b1 = __builtin_amdgcn_perm(in[3], in[2], 0x07030602u);
+  out[0] = __builtin_amdgcn_perm(b0, a0, 0x05040100u);  // r0c0 r1c0 r2c0 r3c0
+  out[1] = __builtin_amdgcn_perm(b0, a0, 0x07060302u);
+  out[2] = __builtin_amdgcn_perm(b1, a1, 0x05040100u);
+  out[3] = __builtin_amdgcn_perm(b1, a1, 0x07060302u);
+}
+
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void cast_kernel(const uint16_t* __restrict__ x, int64_t rows,
+                                                        int64_t cols, int64_t tiles_c,
+                                                        const fp8_scale_t* __restrict__ s,
+                                                        uint8_t* __restrict__ out_row,
+                                                        uint8_t* __restrict__ out_t) {
+  __shared__ uint4 lds[kTile * kTile / 16];  // transposed tile: 128 rows of 128 bytes
+  const int t = threadIdx.x;
+  const int64_t tr = blockIdx.x / tiles_c, tc = blockIdx.x - (blockIdx.x / tiles_c) * tiles_c;
+  const int64_t r0 = tr * kTile, c0 = tc * kTile;
+  const int rg = t >> 4, cc = t & 15;
+  const float scale = s->scale;
+  const bool nonfinite = (s->flags & FP8_FLAG_NONFINITE) != 0u;
+  const int64_t rr = r0 + 8 * rg, cx = c0 + 8 * cc;
+  const bool ok = rr < rows && cx < cols;  // rows, cols are multiples of 16
+
+  uint32_t lo[8], hi[8];
+  if (ok) {
+    const uint16_t* src = x + rr * cols + cx;
+    uint4 v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = *(const uint4*)(src + i * cols);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      lo[i] = cvt4<FMT>(v[i].x, v[i].y, scale);
+      hi[i] = cvt4<FMT>(v[i].z, v[i].w, scale);
+    }
+    if (nonfinite) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        lo[i] = patch_nan(lo[i], v[i].x, v[i].y);
+        hi[i] = patch_nan(hi[i], v[i].z, v[i].w);
+      }
+    }
+    if (out_row) {
+      uint8_t* dst = out_row + rr * cols + cx;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) *(uint2*)(dst + i * cols) = make_uint2(lo[i], hi[i]);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) lo[i] = hi[i] = 0u;
+  }
+  if (!out_t) return;
+
+  // column j of the patch: rows 0-3 in c03[j], rows 4-7 in c47[j]
+  uint32_t c03[8], c47[8];
+  transpose4(&lo[0], &c03[0]);
+  transpose4(&hi[0], &c03[4]);
+  transpose4(&lo[4], &c47[0]);
+  transpose4(&hi[4], &c47[4]);
+  uint8_t* l8 = (uint8_t*)lds;
+  const int sw = cc & 7;  // = (transposed row / 8) & 7
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int trow = 8 * cc + j;
+    const int off = trow * kTile + ((((rg >> 1) ^ sw)) << 4) + 8 * (rg & 1);
+    *(uint2*)(l8 + off) = make_uint2(c03[j], c47[j]);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int q = t + kThreads * k;
+    const int trow = q >> 3, part = q & 7;
+    const uint4 v = lds[trow * 8 + (part ^ ((trow >> 3) & 7))];
+    const int64_t oc = c0 + trow, orow = r0 + 16 * part;
+    if (oc < cols && orow < rows) *(uint4*)(out_t + oc * rows + orow) = v;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_cast(const void* x, int64_t rows, int64_t cols, int fmt, const fp8_scale_t* s,
+                       uint8_t* out_row, uint8_t* out_t, hipStream_t st) {
+  if (rows == 0 || cols == 0 || (!out_row && !out_t)) return hipSuccess;
+  const int64_t tiles_r = (rows + kTile - 1) / kTile, tiles_c = (cols + kTile - 1) / kTile;
+  const dim3 grid((unsigned)(tiles_r * tiles_c));
+  if (fmt == FP8_E4M3)
+    hipLaunchKernelGGL(cast_kernel<FP8_E4M3>, grid, dim3(kThreads), 0, st, (const uint16_t*)x, rows,
+                       cols, tiles_c, s, out_row, out_t);
+  else
+    hipLaunchKernelGGL(cast_kernel<FP8_E5M2>, grid, dim3(kThreads), 0, st, (const uint16_t*)x, rows,
+                       cols, tiles_c, s, out_row, out_t);
+  return hipGetLastError();
+}
+
+}  // namespace fp8lin

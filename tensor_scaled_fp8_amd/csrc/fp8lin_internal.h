@@ -1,0 +1,74 @@
+// Internal declarations shared by the HIP sources of libfp8lin.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fp8lin.h"
+
+namespace fp8lin {
+
+// Largest finite value of each format is 1.75 * 2^kTopExp.
+constexpr int kTopExpE4M3 = 8;   // 448
+constexpr int kTopExpE5M2 = 15;  // 57344
+constexpr int kBiasMin = -126;
+constexpr int kBiasMax = 126;
+constexpr int kIntArgLimit = 1024;
+
+// Scale choice from amax, given as the bit pattern of |amax| in fp32
+// (0..0x7FFFFFFF; a bf16 amax is its 16-bit pattern shifted left by 16):
+//   bias = floor(log2(fmt_max / amax)) - margin + mu_log2, clamped.
+// Writing amax = m * 2^e with m in [1, 2) and fmt_max = 1.75 * 2^E, the
+// floor is E - e when m <= 1.75 and E - e - 1 when m > 1.75, so the rule
+// needs only the exponent and mantissa fields: no floating-point log.
+__host__ __device__ inline int32_t bias_from_amax_bits(uint32_t mag, int fmt, int margin, int mu_log2,
+                                                       uint32_t* flags) {
+  uint32_t f = 0;
+  int32_t b = 0;
+  if (mag >= 0x7F800000u) {
+    f = FP8_FLAG_NONFINITE;
+  } else if (mag == 0u) {
+    f = FP8_FLAG_ZERO;
+  } else {
+    const int top = (fmt == FP8_E5M2) ? kTopExpE5M2 : kTopExpE4M3;
+    const uint32_t ef = mag >> 23, mf = mag & 0x7FFFFFu;
+    int e;
+    bool above;  // significand > 1.75
+    if (ef != 0) {
+      e = (int)ef - 127;
+      above = mf > 0x600000u;  // 1 + mf/2^23 > 1.75
+    } else {
+      // subnormal: mf * 2^-149 = 2^(p-149) * (mf / 2^p), p = highest set bit
+      const int p = 31 - __builtin_clz(mf);
+      e = p - 149;
+      above = 4u * mf > (7u << p);  // mf / 2^p > 1.75
+    }
+    b = top - e - (above ? 1 : 0) - margin + mu_log2;
+    if (b < kBiasMin || b > kBiasMax) {
+      f |= FP8_FLAG_CLAMPED;
+      b = b < kBiasMin ? kBiasMin : kBiasMax;
+    }
+  }
+  if (flags) *flags = f;
+  return b;
+}
+
+__host__ __device__ inline float pow2f(int32_t b) {  // 2^b for b in [-126, 127]
+  union { uint32_t u; float f; } v;
+  v.u = (uint32_t)(b + 127) << 23;
+  return v.f;
+}
+
+// Kernel launchers (defined in the .hip files). They assume validated
+// arguments and return the launch status.
+hipError_t launch_scale_reset(fp8_scale_t* s, int64_t count, hipStream_t st);
+hipError_t launch_amax(const void* x, int64_t n, fp8_scale_t* s, bool fuse_scale, int fmt, int margin,
+                       int mu_log2, hipStream_t st);
+hipError_t launch_scale(fp8_scale_t* s, int fmt, int margin, int mu_log2, hipStream_t st);
+hipError_t launch_cast(const void* x, int64_t rows, int64_t cols, int fmt, const fp8_scale_t* s,
+                       uint8_t* out_row, uint8_t* out_t, hipStream_t st);
+hipError_t launch_gemm(const uint8_t* A, int fa, const fp8_scale_t* sa, const uint8_t* B, int fb,
+                       const fp8_scale_t* sb, int64_t M, int64_t N, int64_t R, void* C,
+                       hipStream_t st);
+
+}  // namespace fp8lin

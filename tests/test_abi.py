@@ -1,0 +1,106 @@
+"""Host-side checks of the C ABI (no GPU needed, no kernel launched):
+the library loads, exports every function include/fp8lin.h declares, the
+host copy of the scale rule equals the oracle's bias for every bf16 amax,
+and argument validation returns the documented status before any launch."""
+import ctypes
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+import tensor_scaled_fp8_amd as tsf
+from tensor_scaled_fp8_amd import _lib
+from oracle import E4M3, E5M2, FLAG_CLAMPED, bf16_to_f64, compute_bias
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8lin.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*[A-Za-z_][\w\s\*]*?\b(fp8_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_header_functions_all_exported():
+    lib = tsf.load()
+    names = _declared_functions()
+    assert len(names) >= 11, names
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in _lib.SIGNATURES, f"binding lacks {n}"
+    assert lib.fp8_abi_version() == 1
+
+
+def test_status_strings():
+    lib = tsf.load()
+    for s in range(4):
+        assert lib.fp8_status_str(s)
+    assert lib.fp8_status_str(99) == b"unknown status"
+
+
+@pytest.mark.parametrize("fmt,name", [(E4M3, "e4m3"), (E5M2, "e5m2")])
+def test_host_bias_rule_matches_oracle_all_bf16(fmt, name):
+    vals = bf16_to_f64(np.arange(0, 0x7F81, dtype=np.uint16))
+    for margin, mu in ((0, 0), (1, 0), (0, 3), (-2, -1)):
+        for a in vals:
+            b, f = tsf.fp8_bias_host(float(a), name, margin, mu)
+            rb, rf = compute_bias(float(a), fmt, margin, mu)
+            assert (b, f) == (rb, rf), (name, a, margin, mu, b, f, rb, rf)
+
+
+def test_host_bias_rule_fp32_amax_and_nan():
+    g = np.random.Generator(np.random.PCG64(1))
+    bits = g.integers(1, 0x7F800000, size=20000, dtype=np.uint32)
+    for a in bits.view(np.float32):
+        for fmt, name in ((E4M3, "e4m3"), (E5M2, "e5m2")):
+            assert tsf.fp8_bias_host(float(a), name) == compute_bias(float(a), fmt)
+    assert tsf.fp8_bias_host(math.nan, "e4m3") == (0, 1)
+    assert tsf.fp8_bias_host(math.inf, "e5m2") == (0, 1)
+    assert tsf.fp8_bias_host(-3.0, "e4m3") == compute_bias(3.0, E4M3)
+
+
+def _vp(x):
+    return ctypes.c_void_p(x)
+
+
+def test_argument_validation_without_launch():
+    lib = tsf.load()
+    ok = 4096                          # a 16-byte aligned non-null fake address (never dereferenced)
+    INV, UNS = _lib.FP8_ERR_INVALID, _lib.FP8_ERR_UNSUPPORTED
+    # null / misaligned / negative / bad enum -> INVALID
+    assert lib.fp8_amax(_vp(ok), -1, _vp(ok), None) == INV
+    assert lib.fp8_amax(_vp(ok), 10, None, None) == INV
+    assert lib.fp8_amax(_vp(ok + 2), 10, _vp(ok), None) == INV
+    assert lib.fp8_scale(7, 0, 0, _vp(ok), None) == INV
+    assert lib.fp8_scale(0, 5000, 0, _vp(ok), None) == INV
+    assert lib.fp8_amax_scale(_vp(ok), 8, 0, 0, -2000, _vp(ok), None) == INV
+    assert lib.fp8_scale_reset(_vp(ok + 8), 1, None) == INV
+    # cast: dims must be multiples of 16
+    assert lib.fp8_cast(_vp(ok), 17, 32, 0, _vp(ok), _vp(ok), None, None) == UNS
+    assert lib.fp8_cast(_vp(ok), 32, 40, 1, _vp(ok), _vp(ok), None, None) == UNS
+    assert lib.fp8_cast(None, 32, 32, 0, _vp(ok), _vp(ok), None, None) == INV
+    assert lib.fp8_cast(_vp(ok), 32, 32, 0, _vp(ok), _vp(ok + 4), None, None) == INV
+    # gemm
+    g = lib.fp8_gemm_nt
+    assert g(_vp(ok), 0, _vp(ok), _vp(ok), 0, _vp(ok), 16, 16, 24, _vp(ok), None) == UNS
+    assert g(_vp(ok), 0, _vp(ok), _vp(ok), 3, _vp(ok), 16, 16, 16, _vp(ok), None) == INV
+    assert g(_vp(ok), 0, None, _vp(ok), 0, _vp(ok), 16, 16, 16, _vp(ok), None) == INV
+    assert g(_vp(ok), 0, _vp(ok), _vp(ok), 0, _vp(ok), -16, 16, 16, _vp(ok), None) == INV
+    assert g(_vp(ok), 0, _vp(ok), None, 0, _vp(ok), 16, 16, 16, _vp(ok), None) == INV
+    # linear: workspace checks
+    ws = _lib.LinearWs(ok, ok, ok, ok, ok, ok, ok, ok, ok)
+    assert lib.fp8_linear_fwd(_vp(ok), _vp(ok), 16, 16, 16, 0, None, _vp(ok), None) == INV
+    assert lib.fp8_linear_fwd(_vp(ok), _vp(ok), 16, 24, 16, 0, ctypes.byref(ws), _vp(ok), None) == UNS
+    ws_bad = _lib.LinearWs(ok, ok, ok, ok, None, ok, ok, ok, ok)
+    assert lib.fp8_linear_bwd(_vp(ok), 16, 16, 16, 0, 0, ctypes.byref(ws_bad), None, None, None) == INV
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    x = torch.zeros(16, 16, dtype=torch.bfloat16)
+    s = torch.zeros(8, dtype=torch.int32)
+    with pytest.raises(ValueError, match="device tensor"):
+        tsf.fp8_amax(x, s)
