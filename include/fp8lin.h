@@ -75,10 +75,11 @@ typedef enum fp8_status {
  *   scale     2^b: multiplies the tensor before the FP8 cast [AMAX bullet 3].
  *   scale_inv 2^-b: undoes the scale after the GEMM.
  *   flags     FP8_FLAG_* bits.
- * The two reduce_* words are the amax reduction's working state. They must
- * be zero before the first fp8_amax / fp8_amax_scale call on the record
- * (allocate zeroed memory or call fp8_scale_reset once); every such call
- * leaves them zero again when it completes.
+ * reduce_bits is the amax reduction's working word (blocks merge their
+ * maxima into it with device-scope atomics); reduce_ticket is reserved.
+ * Both must be zero before the first fp8_amax / fp8_amax_scale call on
+ * the record (allocate zeroed memory or call fp8_scale_reset once); every
+ * such call leaves them zero again when its work on the stream completes.
  */
 typedef struct fp8_scale_t {
   float amax;
@@ -87,7 +88,7 @@ typedef struct fp8_scale_t {
   float scale_inv;
   uint32_t flags;
   uint32_t reduce_bits;   /* internal: running max of the |bf16| bit patterns */
-  uint32_t reduce_ticket; /* internal: count of finished reduction blocks */
+  uint32_t reduce_ticket; /* internal: reserved, kept zero */
   uint32_t reserved;
 } fp8_scale_t;
 
@@ -121,7 +122,8 @@ fp8_status fp8_amax(const void* x_bf16, int64_t n, fp8_scale_t* s_dev, hipStream
  */
 fp8_status fp8_scale(fp8_fmt fmt, int margin, int mu_log2, fp8_scale_t* s_dev, hipStream_t stream);
 
-/* a1 + a2 in one kernel launch (the last reduction block picks the scale). */
+/* a1 + a2 fused: one reduction pass, then a one-thread kernel that writes
+ * amax, bias, scale, scale_inv and flags (no separate fp8_scale call). */
 fp8_status fp8_amax_scale(const void* x_bf16, int64_t n, fp8_fmt fmt, int margin, int mu_log2,
                           fp8_scale_t* s_dev, hipStream_t stream);
 
@@ -153,7 +155,8 @@ fp8_status fp8_cast(const void* x_bf16, int64_t rows, int64_t cols, fp8_fmt fmt,
  *   B   device, [N, R] u8 codes of format fb, row-major (r contiguous).
  *   C   device, [M, N] bf16 row-major (overwritten).
  *   sa, sb  device scaling records of A and B.
- *   M, N, R >= 0 and multiples of 16 (else FP8_ERR_UNSUPPORTED); R = 0 gives C = 0.
+ *   M, N, R >= 0 and multiples of 16, and A and B each below 4 GiB
+ *   (M*R, N*R < 2^32), else FP8_ERR_UNSUPPORTED; R = 0 gives C = 0.
  *   Forward:  Y  = gemm(A = x8 [M,K],  B = w8t [N,K])
  *   Dgrad:    dX = gemm(A = dy8 [M,N], B = w8 [K,N])      (E5M2 x E4M3)
  *   Wgrad:    dW = gemm(A = x8t [K,M], B = dy8t [N,M])    (E4M3 x E5M2)
@@ -186,7 +189,8 @@ typedef struct fp8_linear_ws {
  * Forward of one linear, Y = X W: amax+scale of X and W (E4M3), cast
  * (+transpose) of both, then the forward GEMM.
  *   X [M,K] bf16, W [K,N] bf16 (in x out), Y [M,N] bf16; device, 16-B aligned.
- *   M, K, N multiples of 16. ws: host struct of device pointers (above).
+ *   M, K, N multiples of 16, every FP8 operand below 4 GiB. ws: host struct
+ *   of device pointers (above).
  */
 fp8_status fp8_linear_fwd(const void* X, const void* W, int64_t M, int64_t K, int64_t N, int margin,
                           const fp8_linear_ws* ws, void* Y, hipStream_t stream);

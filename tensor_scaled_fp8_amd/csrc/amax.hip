@@ -1,15 +1,20 @@
-// a1 amax (+ fused a2 scale choice) over a bf16 tensor.
+// a1 amax (+ a2 scale choice) over a bf16 tensor.
 //
 // [Perez et al. review, "Proposed method", bullets 1-2] the scaling bias of
-// a tensor comes from its max |x|. One pass over HBM with 16-byte loads.
-// |x| is compared on the 15-bit magnitude pattern: for bf16, integer order
-// of (bits & 0x7FFF) is the order of |x|, with inf above every finite value
-// and NaN patterns above inf, so the integer max also detects non-finite
-// values. Two packed 16-bit maxima per dword (one VALU op per two values),
-// a wavefront max by cross-lane exchange, a block max through LDS, then one
-// device-scope atomic max per block. The block that finishes last (ticket
-// counter) publishes amax and, when fused, the scale; it leaves the
-// reduction words at zero for the next call.
+// a tensor comes from its max |x|. One pass over HBM with 16-byte
+// nontemporal loads (streamed past the caches, which keeps reads near the
+// HBM rate). |x| is compared on the 15-bit magnitude pattern: for bf16,
+// the integer order of (bits & 0x7FFF) is the order of |x|, with inf above
+// every finite value and NaN patterns above inf, so the integer max also
+// detects non-finite values. Two packed 16-bit maxima per dword (one VALU
+// op per two values), a wavefront max by cross-lane exchange, a block max
+// through LDS. Each block then merges into the record's reduction word
+// with a device-scope atomic max, but only when its value exceeds what the
+// word already holds: same-address atomics from thousands of blocks
+// serialise, and after the first few blocks almost none is needed. A
+// one-thread kernel on the same stream then publishes amax (and the scale)
+// and clears the reduction word for the next call; the launch boundary
+// orders it after every block's atomic.
 #include "fp8lin_internal.h"
 
 namespace fp8lin {
@@ -17,9 +22,11 @@ namespace {
 
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
 constexpr int kThreads = 256;
 constexpr int kUnroll = 8;         // 16-byte loads in flight per thread
-constexpr int kMaxBlocks = 2048;   // 8 blocks per CU on 256 CUs
+constexpr int kMaxBlocks = 1024;   // 4 blocks per CU on 256 CUs
 
 __device__ inline u16x2 as_u16x2(uint32_t v) { return __builtin_bit_cast(u16x2, v); }
 __device__ inline uint32_t as_u32(u16x2 v) { return __builtin_bit_cast(uint32_t, v); }
@@ -46,18 +53,19 @@ __device__ inline void write_scale(fp8_scale_t* s, uint32_t mag, bool fuse, int 
   s->flags = flags;
 }
 
-__global__ __launch_bounds__(kThreads) void amax_kernel(const uint4* __restrict__ x, int64_t n_vec,
+__global__ __launch_bounds__(kThreads) void amax_kernel(const u32x4* __restrict__ x, int64_t n_vec,
+                                                        int64_t per_block,
                                                         const uint16_t* __restrict__ tail,
-                                                        int tail_n, fp8_scale_t* s, int fuse,
-                                                        int fmt, int margin, int mu_log2) {
+                                                        int tail_n, fp8_scale_t* s) {
   u16x2 m = {0, 0};
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  // main sweep: kUnroll independent loads per iteration
-  for (; i + (kUnroll - 1) * stride < n_vec; i += kUnroll * stride) {
-    uint4 v[kUnroll];
+  // block-contiguous chunk, kUnroll * 256 consecutive 16-byte vectors per step
+  const int64_t b0 = (int64_t)blockIdx.x * per_block;
+  const int64_t b1 = b0 + per_block < n_vec ? b0 + per_block : n_vec;
+  int64_t base = b0;
+  for (; base + kUnroll * kThreads <= b1; base += kUnroll * kThreads) {
+    u32x4 v[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) v[u] = x[i + u * stride];
+    for (int u = 0; u < kUnroll; ++u) v[u] = __builtin_nontemporal_load(x + base + u * kThreads + threadIdx.x);
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       m = vmax(m, v[u].x);
@@ -66,8 +74,8 @@ __global__ __launch_bounds__(kThreads) void amax_kernel(const uint4* __restrict_
       m = vmax(m, v[u].w);
     }
   }
-  for (; i < n_vec; i += stride) {
-    uint4 v = x[i];
+  for (int64_t i = base + threadIdx.x; i < b1; i += kThreads) {
+    const u32x4 v = __builtin_nontemporal_load(x + i);
     m = vmax(m, v.x);
     m = vmax(m, v.y);
     m = vmax(m, v.z);
@@ -84,7 +92,6 @@ __global__ __launch_bounds__(kThreads) void amax_kernel(const uint4* __restrict_
     r = o > r ? o : r;
   }
   __shared__ uint32_t wmax[kThreads / 64];
-  __shared__ int last;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   if (lane == 0) wmax[wid] = r;
   __syncthreads();
@@ -92,18 +99,17 @@ __global__ __launch_bounds__(kThreads) void amax_kernel(const uint4* __restrict_
     uint32_t b = wmax[0];
 #pragma unroll
     for (int w = 1; w < kThreads / 64; ++w) b = wmax[w] > b ? wmax[w] : b;
-    if (b != 0u) atomicMax(&s->reduce_bits, b);
-    __threadfence();
-    const uint32_t t = atomicAdd(&s->reduce_ticket, 1u);
-    last = (t == gridDim.x - 1);
+    const uint32_t seen = __hip_atomic_load(&s->reduce_bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (b > seen) atomicMax(&s->reduce_bits, b);
   }
-  __syncthreads();
-  if (last && threadIdx.x == 0) {
-    __threadfence();
-    const uint32_t mag = atomicExch(&s->reduce_bits, 0u);
-    atomicExch(&s->reduce_ticket, 0u);
-    write_scale(s, mag, fuse != 0, fmt, margin, mu_log2);
-  }
+}
+
+// Publishes the reduced amax (and, when fused, the scale) and clears the
+// reduction word. One thread; runs after amax_kernel on the same stream.
+__global__ void amax_finish_kernel(fp8_scale_t* s, int fuse, int fmt, int margin, int mu_log2) {
+  const uint32_t mag = atomicExch(&s->reduce_bits, 0u);
+  s->reduce_ticket = 0u;
+  write_scale(s, mag, fuse != 0, fmt, margin, mu_log2);
 }
 
 __global__ void scale_kernel(fp8_scale_t* s, int fmt, int margin, int mu_log2) {
@@ -137,10 +143,18 @@ hipError_t launch_amax(const void* x, int64_t n, fp8_scale_t* s, bool fuse_scale
   const int64_t n_vec = n / 8;
   const int tail_n = (int)(n - n_vec * 8);
   const uint16_t* tail = (const uint16_t*)x + n_vec * 8;
-  int64_t want = (n_vec + (int64_t)kThreads * kUnroll - 1) / ((int64_t)kThreads * kUnroll);
-  int blocks = (int)(want < 1 ? 1 : (want > kMaxBlocks ? kMaxBlocks : want));
-  hipLaunchKernelGGL(amax_kernel, dim3(blocks), dim3(kThreads), 0, st, (const uint4*)x, n_vec, tail,
-                     tail_n, s, fuse_scale ? 1 : 0, fmt, margin, mu_log2);
+  // enough blocks to fill the chip, each a contiguous chunk of whole steps
+  const int64_t step = (int64_t)kThreads * kUnroll;
+  int64_t blocks = (n_vec + step - 1) / step;
+  blocks = blocks < 1 ? 1 : (blocks > kMaxBlocks ? kMaxBlocks : blocks);
+  const int64_t per_block = ((n_vec + blocks - 1) / blocks + step - 1) / step * step;
+  blocks = n_vec > 0 ? (n_vec + per_block - 1) / per_block : 1;
+  hipLaunchKernelGGL(amax_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, st, (const u32x4*)x, n_vec,
+                     per_block, tail, tail_n, s);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(amax_finish_kernel, dim3(1), dim3(1), 0, st, s, fuse_scale ? 1 : 0, fmt, margin,
+                     mu_log2);
   return hipGetLastError();
 }
 

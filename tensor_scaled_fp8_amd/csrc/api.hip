@@ -13,6 +13,11 @@ inline bool fmt_ok(int f) { return f == FP8_E4M3 || f == FP8_E5M2; }
 inline bool int_ok(int v) { return v >= -kIntArgLimit && v <= kIntArgLimit; }
 constexpr int64_t kMaxDim = (int64_t)1 << 31;  // per-dimension limit (tile indices are 32-bit)
 inline fp8_status hip_status(hipError_t e) { return e == hipSuccess ? FP8_OK : FP8_ERR_HIP; }
+// GEMM operands are addressed with 32-bit byte offsets
+constexpr int64_t kMaxOperandBytes = (int64_t)1 << 32;
+inline bool gemm_fits(int64_t M, int64_t N, int64_t R) {
+  return M * R < kMaxOperandBytes && N * R < kMaxOperandBytes;
+}
 
 }  // namespace
 
@@ -83,7 +88,7 @@ fp8_status fp8_gemm_nt(const uint8_t* A, fp8_fmt fa, const fp8_scale_t* sa, cons
                        void* C_bf16, hipStream_t stream) {
   if (M < 0 || N < 0 || R < 0 || !fmt_ok(fa) || !fmt_ok(fb)) return FP8_ERR_INVALID;
   if (!sa || !sb || !aligned16(sa) || !aligned16(sb)) return FP8_ERR_INVALID;
-  if (M % 16 || N % 16 || R % 16 || M >= kMaxDim || N >= kMaxDim || R >= kMaxDim)
+  if (M % 16 || N % 16 || R % 16 || M >= kMaxDim || N >= kMaxDim || R >= kMaxDim || !gemm_fits(M, N, R))
     return FP8_ERR_UNSUPPORTED;
   if (M > 0 && N > 0) {
     if (!C_bf16 || !aligned16(C_bf16)) return FP8_ERR_INVALID;
@@ -108,7 +113,8 @@ static fp8_status check_ws(const fp8_linear_ws* ws, bool fwd) {
 fp8_status fp8_linear_fwd(const void* X, const void* W, int64_t M, int64_t K, int64_t N, int margin,
                           const fp8_linear_ws* ws, void* Y, hipStream_t stream) {
   if (M < 0 || K < 0 || N < 0 || !int_ok(margin)) return FP8_ERR_INVALID;
-  if (M % 16 || K % 16 || N % 16 || M >= kMaxDim || K >= kMaxDim || N >= kMaxDim)
+  if (M % 16 || K % 16 || N % 16 || M >= kMaxDim || K >= kMaxDim || N >= kMaxDim ||
+      !gemm_fits(M, N, K) || !gemm_fits(K, N, M))
     return FP8_ERR_UNSUPPORTED;
   fp8_status st = check_ws(ws, true);
   if (st != FP8_OK) return st;
@@ -126,7 +132,8 @@ fp8_status fp8_linear_fwd(const void* X, const void* W, int64_t M, int64_t K, in
 fp8_status fp8_linear_bwd(const void* dY, int64_t M, int64_t K, int64_t N, int margin, int mu_log2,
                           const fp8_linear_ws* ws, void* dX, void* dW, hipStream_t stream) {
   if (M < 0 || K < 0 || N < 0 || !int_ok(margin) || !int_ok(mu_log2)) return FP8_ERR_INVALID;
-  if (M % 16 || K % 16 || N % 16 || M >= kMaxDim || K >= kMaxDim || N >= kMaxDim)
+  if (M % 16 || K % 16 || N % 16 || M >= kMaxDim || K >= kMaxDim || N >= kMaxDim ||
+      !gemm_fits(M, K, N) || !gemm_fits(K, N, M))
     return FP8_ERR_UNSUPPORTED;
   fp8_status st = check_ws(ws, false);
   if (st != FP8_OK) return st;

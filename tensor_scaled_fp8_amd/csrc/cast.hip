@@ -9,6 +9,7 @@
 // subnormals. NaN inputs (only possible when the tensor's record carries
 // FP8_FLAG_NONFINITE) are patched to 0x7F|sign afterwards.
 //
+// Inputs are read with nontemporal loads (streamed past the caches).
 // Tiling: one 256-thread block per 128 x 128 tile. Each thread loads an
 // 8 x 8 patch (eight 16-byte row loads), converts it, stores its eight
 // 8-byte row-wise pieces, transposes the 8 x 8 bytes in registers
@@ -21,6 +22,8 @@
 
 namespace fp8lin {
 namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kTile = 128;
 constexpr int kThreads = 256;
@@ -92,9 +95,9 @@ __global__ __launch_bounds__(kThreads) void cast_kernel(const uint16_t* __restri
   uint32_t lo[8], hi[8];
   if (ok) {
     const uint16_t* src = x + rr * cols + cx;
-    uint4 v[8];
+    u32x4 v[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = *(const uint4*)(src + i * cols);
+    for (int i = 0; i < 8; ++i) v[i] = __builtin_nontemporal_load((const u32x4*)(src + i * cols));
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       lo[i] = cvt4<FMT>(v[i].x, v[i].y, scale);
