@@ -42,11 +42,13 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=2, help="layer workload index (1-5)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=256, help="token rows of the CPU oracle sample")
-    ap.add_argument("--cpu-cols", type=int, default=2048, help="output features of the CPU oracle sample")
+    ap.add_argument("--cpu-rows", type=int, default=512, help="token rows of the CPU oracle sample")
+    ap.add_argument("--cpu-cols", type=int, default=6144, help="output features of the CPU oracle sample")
     ap.add_argument("--check", action="store_true", help="check sampled outputs against the oracle")
-    ap.add_argument("--traffic", default=None,
+    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "gemm_traffic_gpt7b-layer.json"),
                     help="JSON file with measured per-launch HBM bytes of the GEMM kernel")
+    ap.add_argument("--calibration-copy", type=int, default=0,
+                    help="bytes of one plain device copy run before timing (PMC calibration)")
     return ap.parse_args()
 
 
@@ -122,6 +124,13 @@ def main():
                 else:
                     fn()
 
+    if args.calibration_copy:
+        n = args.calibration_copy
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         step(False)
     torch.cuda.synchronize()
@@ -143,10 +152,7 @@ def main():
         a["n"] += 1
     g = agg["gemm"]
     gemm_tflops = g["flops"] / (g["ms"] * 1e-3) / 1e12
-    traffic = None
-    if args.traffic and os.path.exists(args.traffic):
-        with open(args.traffic) as f:
-            traffic = json.load(f).get("gemm_bytes_per_launch")
+    traffic = gemm_traffic(args.traffic)
     roofline = {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": PEAK_FP8_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4), "traffic": traffic,
                 "kernel": "gemm_nt_kernel (FP8 MFMA)",
@@ -190,6 +196,23 @@ def main():
     if check is not None:
         out["check"] = check
     print(json.dumps(out), flush=True)
+
+
+def gemm_traffic(path):
+    """Measured HBM bytes per GEMM launch from a committed counter summary,
+    reported only while the GEMM source is the one the counters were taken
+    on (sha256 of gemm.hip recorded in the summary)."""
+    import hashlib
+    if not path or not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    src = os.path.join(ROOT, "tensor_scaled_fp8_amd", "csrc", "gemm.hip")
+    with open(src, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    if rec.get("gemm_source_sha256") != sha:
+        return None
+    return round(rec["gemm_bytes_per_launch"])
 
 
 def sampled_check(lin, wl, margin, mu):
