@@ -5,20 +5,20 @@ linears, forward + backward, on one MI355X.
 A step runs, for every linear of the layer (default: the GPT-7B-style
 layer, 4096 tokens, hidden 4096: qkv 4096->12288, proj 4096->4096,
 up 4096->16384, down 16384->4096):
-    amax+scale(X), amax+scale(W)        (E4M3)
-    cast+transpose(X), cast+transpose(W)
+    quantize(X), quantize(W)   amax + scale + cast/transpose (E4M3)
     Y  = FP8 GEMM (x8, w8t)
-    amax+scale(dY)                       (E5M2)
-    cast+transpose(dY)
+    quantize(dY)               (E5M2)
     dX = FP8 GEMM (dy8, w8),  dW = FP8 GEMM (x8t, dy8t)
-through the C ABI of libfp8lin.so, with inputs resident in HBM.
+through the C ABI of libfp8lin.so (the launches fp8_linear_fwd/bwd make),
+with inputs resident in HBM.
 
 Prints ONE JSON line: value = sum over linears of 6*M*K*N / step time
-(TFLOP/s). HIP events around every kernel launch of the timed steps give
-the per-kernel durations; `roofline` reports the FP8 GEMM kernel (the
-dominant one) against the dense FP8 MFMA peak, and `kernels` the amax and
-cast kernels against HBM bandwidth. `cpu_baseline` times the oracle on a
-bounded token sample of the same layer on the host cores."""
+(TFLOP/s). HIP events (fence-free) around every GEMM launch of the timed
+steps give the GEMM durations: `roofline` reports the FP8 GEMM kernel (the
+dominant one) against the dense FP8 MFMA peak. A short extra pass with
+events around every launch gives the amax and cast figures (`kernels`,
+against HBM bandwidth). `cpu_baseline` times the oracle on a bounded
+sample of the same layer on the host cores."""
 from __future__ import annotations
 
 import argparse
@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=512, help="token rows of the CPU oracle sample")
     ap.add_argument("--cpu-cols", type=int, default=6144, help="output features of the CPU oracle sample")
     ap.add_argument("--check", action="store_true", help="check sampled outputs against the oracle")
+    ap.add_argument("--breakdown-steps", type=int, default=3,
+                    help="extra steps with events around every launch (amax/cast figures)")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "gemm_traffic_gpt7b-layer.json"),
                     help="JSON file with measured per-launch HBM bytes of the GEMM kernel")
     ap.add_argument("--calibration-copy", type=int, default=0,
@@ -89,38 +91,36 @@ def main():
     t_gen = time.perf_counter() - t_gen
     margin, mu = wl.margin, wl.mu_log2
 
-    # kernel-level step: the same launches fp8_linear_fwd/bwd make, with an
-    # event pair around each so per-kernel durations come from the timed run
+    # kernel-level step: the same launches fp8_linear_fwd/bwd make. Timing
+    # events are HIP events created once, without the system-scope fence on
+    # record (a fenced timing event writes back and invalidates the caches
+    # and measurably slows the kernels around it).
+    hip = HipEvents(torch.cuda.current_stream(dev).cuda_stream)
     events = []
 
-    def ev():
-        e = torch.cuda.Event(enable_timing=True)
-        e.record()
-        return e
-
-    def step(record: bool):
+    def step(instrument):
+        """instrument: None, "gemm" (events around the GEMM launches) or "all"."""
         for d in lin:
             L, ws = d["L"], d["ws"]
             seq = [
-                ("amax", 2 * L.M * L.K, 0, lambda: tsf.fp8_amax_scale(d["X"], "e4m3", ws.sx, margin)),
-                ("amax", 2 * L.K * L.N, 0, lambda: tsf.fp8_amax_scale(d["W"], "e4m3", ws.sw, margin)),
-                ("cast", 4 * L.M * L.K, 0, lambda: tsf.fp8_cast(d["X"], "e4m3", ws.sx, ws.x8, ws.x8t)),
-                ("cast", 4 * L.K * L.N, 0, lambda: tsf.fp8_cast(d["W"], "e4m3", ws.sw, ws.w8, ws.w8t)),
+                ("quant", 6 * L.M * L.K, 0,
+                 lambda: tsf.fp8_quantize(d["X"], "e4m3", ws.sx, margin, 0, ws.x8, ws.x8t)),
+                ("quant", 6 * L.K * L.N, 0,
+                 lambda: tsf.fp8_quantize(d["W"], "e4m3", ws.sw, margin, 0, ws.w8, ws.w8t)),
                 ("gemm", 0, 2 * L.M * L.N * L.K,
                  lambda: tsf.fp8_gemm_nt(ws.x8, "e4m3", ws.sx, ws.w8t, "e4m3", ws.sw, d["Y"])),
-                ("amax", 2 * L.M * L.N, 0,
-                 lambda: tsf.fp8_amax_scale(d["dY"], "e5m2", ws.sdy, margin, mu)),
-                ("cast", 4 * L.M * L.N, 0, lambda: tsf.fp8_cast(d["dY"], "e5m2", ws.sdy, ws.dy8, ws.dy8t)),
+                ("quant", 6 * L.M * L.N, 0,
+                 lambda: tsf.fp8_quantize(d["dY"], "e5m2", ws.sdy, margin, mu, ws.dy8, ws.dy8t)),
                 ("gemm", 0, 2 * L.M * L.K * L.N,
                  lambda: tsf.fp8_gemm_nt(ws.dy8, "e5m2", ws.sdy, ws.w8, "e4m3", ws.sw, d["dX"])),
                 ("gemm", 0, 2 * L.K * L.N * L.M,
                  lambda: tsf.fp8_gemm_nt(ws.x8t, "e4m3", ws.sx, ws.dy8t, "e5m2", ws.sdy, d["dW"])),
             ]
             for kind, nbytes, flops, fn in seq:
-                if record:
-                    e0 = ev()
+                if instrument == "all" or (instrument == "gemm" and kind == "gemm"):
+                    e0 = hip.record()
                     fn()
-                    events.append((kind, nbytes, flops, e0, ev()))
+                    events.append((kind, nbytes, flops, e0, hip.record()))
                 else:
                     fn()
 
@@ -132,43 +132,57 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     for _ in range(args.warmup):
-        step(False)
+        step(None)
+    hip.reserve(2 * 3 * len(lin) * args.steps + 2 * 6 * len(lin) * args.breakdown_steps)
+    # timed region: K whole steps; events bracket every GEMM launch
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step(True)
+        step("gemm")
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms = (t1 - t0) * 1e3 / args.steps
     flops = wl.flops_fwd_bwd()
     value = flops / (ms * 1e-3) / 1e12
+    timed = [(k, b, f, hip.elapsed_ms(e0, e1)) for k, b, f, e0, e1 in events]
+    # breakdown pass: the same steps with events around every launch (amax
+    # and cast figures; these events cost a little time, so this pass is
+    # kept out of the timed region)
+    events.clear()
+    for _ in range(args.breakdown_steps):
+        step("all")
+    torch.cuda.synchronize()
+    brk = [(k, b, f, hip.elapsed_ms(e0, e1)) for k, b, f, e0, e1 in events]
 
-    agg = {}
-    for kind, nbytes, fl, e0, e1 in events:
-        a = agg.setdefault(kind, {"ms": 0.0, "bytes": 0, "flops": 0, "n": 0})
-        a["ms"] += e0.elapsed_time(e1)
-        a["bytes"] += nbytes
-        a["flops"] += fl
-        a["n"] += 1
-    g = agg["gemm"]
+    def aggregate(rows):
+        agg = {}
+        for kind, nbytes, fl, t in rows:
+            a = agg.setdefault(kind, {"ms": 0.0, "bytes": 0, "flops": 0, "n": 0})
+            a["ms"] += t
+            a["bytes"] += nbytes
+            a["flops"] += fl
+            a["n"] += 1
+        return agg
+
+    g = aggregate(timed)["gemm"]
     gemm_tflops = g["flops"] / (g["ms"] * 1e-3) / 1e12
     traffic = gemm_traffic(args.traffic)
     roofline = {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": PEAK_FP8_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4), "traffic": traffic,
                 "kernel": "gemm_nt_kernel (FP8 MFMA)",
                 "avg_launch_us": round(g["ms"] * 1e3 / g["n"], 2)}
+    agg = aggregate(brk)
     kernels = {}
-    for kind in ("amax", "cast"):
-        a = agg[kind]
-        gbs = a["bytes"] / (a["ms"] * 1e-3) / 1e9
-        kernels[kind] = {"GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
-                         "ms_per_step": round(a["ms"] / args.steps, 4),
-                         "avg_launch_us": round(a["ms"] * 1e3 / a["n"], 2)}
-    qa = agg["amax"]["bytes"] + agg["cast"]["bytes"]
-    qms = agg["amax"]["ms"] + agg["cast"]["ms"]
-    kernels["amax+cast"] = {"GB/s": round(qa / (qms * 1e-3) / 1e9, 1),
-                            "frac_hbm": round(qa / (qms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    a = agg["quant"]
+    gbs = a["bytes"] / (a["ms"] * 1e-3) / 1e9
+    kernels["amax+cast"] = {"GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
+                            "ms_per_step": round(a["ms"] / args.breakdown_steps, 4),
+                            "avg_call_us": round(a["ms"] * 1e3 / a["n"], 2),
+                            "bytes": "6 per element: amax read 2, cast read 2, two FP8 copies 2"}
     kernels["gemm"] = {"TFLOP/s": round(gemm_tflops, 1), "ms_per_step": round(g["ms"] / args.steps, 4)}
+    kernels["note"] = ("gemm: events in the timed region; amax+cast (fp8_quantize: amax pass + "
+                       f"cast kernel): a separate pass of {args.breakdown_steps} steps with events "
+                       "around every call")
 
     check = None
     if args.check:
@@ -196,6 +210,54 @@ def main():
     if check is not None:
         out["check"] = check
     print(json.dumps(out), flush=True)
+
+
+class HipEvents:
+    """Timing events of the HIP runtime the process already uses, created
+    with hipEventDisableSystemFence, recorded on one stream."""
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self, stream: int):
+        import ctypes
+        path = None
+        with open("/proc/self/maps") as f:
+            for line in f:
+                if "libamdhip64.so" in line:
+                    path = line.split()[-1]
+                    break
+        if path is None:
+            raise RuntimeError("HIP runtime not loaded")
+        self.ct = ctypes
+        self.lib = ctypes.CDLL(path)   # already loaded: same runtime instance
+        self.lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.stream = ctypes.c_void_p(stream)
+        self.pool = []
+        self.next = 0
+
+    def reserve(self, n):
+        while len(self.pool) < n:
+            e = self.ct.c_void_p()
+            if self.lib.hipEventCreateWithFlags(self.ct.byref(e), self.DISABLE_SYSTEM_FENCE) != 0:
+                raise RuntimeError("hipEventCreateWithFlags failed")
+            self.pool.append(e)
+
+    def record(self):
+        if self.next >= len(self.pool):
+            self.reserve(self.next + 64)
+        e = self.pool[self.next]
+        self.next += 1
+        if self.lib.hipEventRecord(e, self.stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
+        return e
+
+    def elapsed_ms(self, e0, e1):
+        t = self.ct.c_float()
+        if self.lib.hipEventElapsedTime(self.ct.byref(t), e0, e1) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return t.value
 
 
 def gemm_traffic(path):

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define FP8LIN_ABI_VERSION 1
+#define FP8LIN_ABI_VERSION 2
 
 typedef enum fp8_fmt {
   FP8_E4M3 = 0, /* OCP E4M3FN: weights and activations [AMAX bullet 4] */
@@ -66,20 +66,22 @@ typedef enum fp8_status {
 #define FP8_FLAG_CLAMPED 4u   /* the bias rule left [-126, 126] and was clamped */
 
 /*
- * Per-tensor scaling record. Lives in DEVICE memory, 32 bytes, 16-byte
+ * Per-tensor scaling record. Lives in DEVICE memory, 64 bytes, 16-byte
  * aligned. The public fields are written by fp8_amax / fp8_scale /
- * fp8_amax_scale and read by fp8_cast and fp8_gemm_nt.
+ * fp8_amax_scale / fp8_quantize and read by fp8_cast and fp8_gemm_nt.
  *   amax      max |t| over the tensor (a bf16 value widened to fp32); NaN if
  *             the tensor holds a NaN, +inf if it holds an inf and no NaN.
  *   bias      the integer exponent bias b [AMAX bullet 2].
  *   scale     2^b: multiplies the tensor before the FP8 cast [AMAX bullet 3].
  *   scale_inv 2^-b: undoes the scale after the GEMM.
  *   flags     FP8_FLAG_* bits.
- * reduce_bits is the amax reduction's working word (blocks merge their
- * maxima into it with device-scope atomics); reduce_ticket is reserved.
- * Both must be zero before the first fp8_amax / fp8_amax_scale call on
- * the record (allocate zeroed memory or call fp8_scale_reset once); every
- * such call leaves them zero again when its work on the stream completes.
+ * reduce_bits and reduce_ticket are the working words of fp8_amax /
+ * fp8_amax_scale (blocks merge their maxima with device-scope atomics and
+ * count themselves; the last one publishes). gen_max is the working word
+ * of fp8_quantize: (call generation << 16) | bf16 magnitude bits, merged by
+ * atomic max, so a newer call always outranks what an older one left and
+ * the word is never cleared. All three must be zero before the first call
+ * on the record (allocate zeroed memory or call fp8_scale_reset once).
  */
 typedef struct fp8_scale_t {
   float amax;
@@ -88,8 +90,10 @@ typedef struct fp8_scale_t {
   float scale_inv;
   uint32_t flags;
   uint32_t reduce_bits;   /* internal: running max of the |bf16| bit patterns */
-  uint32_t reduce_ticket; /* internal: reserved, kept zero */
+  uint32_t reduce_ticket; /* internal: count of blocks that have merged */
   uint32_t reserved;
+  uint64_t gen_max;       /* internal: generation-tagged running max (fp8_quantize) */
+  uint64_t reserved2[3];
 } fp8_scale_t;
 
 /* Human-readable name of a status. Never NULL. */
@@ -122,8 +126,8 @@ fp8_status fp8_amax(const void* x_bf16, int64_t n, fp8_scale_t* s_dev, hipStream
  */
 fp8_status fp8_scale(fp8_fmt fmt, int margin, int mu_log2, fp8_scale_t* s_dev, hipStream_t stream);
 
-/* a1 + a2 fused: one reduction pass, then a one-thread kernel that writes
- * amax, bias, scale, scale_inv and flags (no separate fp8_scale call). */
+/* a1 + a2 fused in one launch: the last reduction block writes amax, bias,
+ * scale, scale_inv and flags (no separate fp8_scale call). */
 fp8_status fp8_amax_scale(const void* x_bf16, int64_t n, fp8_fmt fmt, int margin, int mu_log2,
                           fp8_scale_t* s_dev, hipStream_t stream);
 
@@ -133,6 +137,19 @@ fp8_status fp8_amax_scale(const void* x_bf16, int64_t n, fp8_fmt fmt, int margin
  * Out-of-range margin/mu_log2 are clamped to +-1024.
  */
 int32_t fp8_bias_host(float amax, fp8_fmt fmt, int margin, int mu_log2, uint32_t* flags_out);
+
+/*
+ * a1 + a2 + a3 fused (the hot path of fp8_linear_fwd / fp8_linear_bwd):
+ * amax of x, the scale rule, and the cast (+ transpose), in two kernel
+ * launches. The amax pass ends without any cross-block handshake; the cast
+ * kernel derives the bias from the merged maximum itself and writes the
+ * record's public fields, so the result equals fp8_amax_scale followed by
+ * fp8_cast. Arguments as for those two calls (x [rows, cols] bf16, rows and
+ * cols multiples of 16; out_rowwise / out_transposed nullable).
+ */
+fp8_status fp8_quantize(const void* x_bf16, int64_t rows, int64_t cols, fp8_fmt fmt, int margin,
+                        int mu_log2, fp8_scale_t* s_dev, uint8_t* out_rowwise, uint8_t* out_transposed,
+                        hipStream_t stream);
 
 /*
  * a3 - cast (+ transpose) [AMAX bullets 3-4]: q = enc_fmt(x * 2^bias) with
@@ -186,8 +203,8 @@ typedef struct fp8_linear_ws {
 } fp8_linear_ws;
 
 /*
- * Forward of one linear, Y = X W: amax+scale of X and W (E4M3), cast
- * (+transpose) of both, then the forward GEMM.
+ * Forward of one linear, Y = X W: fp8_quantize of X and W (E4M3), then the
+ * forward GEMM.
  *   X [M,K] bf16, W [K,N] bf16 (in x out), Y [M,N] bf16; device, 16-B aligned.
  *   M, K, N multiples of 16, every FP8 operand below 4 GiB. ws: host struct
  *   of device pointers (above).
@@ -196,9 +213,9 @@ fp8_status fp8_linear_fwd(const void* X, const void* W, int64_t M, int64_t K, in
                           const fp8_linear_ws* ws, void* Y, hipStream_t stream);
 
 /*
- * Backward of one linear: amax+scale of dY (E5M2, with mu = 2^mu_log2),
- * cast (+transpose) of dY, then dX = dY W^T and dW = X^T dY from the FP8
- * copies the forward left in ws.
+ * Backward of one linear: fp8_quantize of dY (E5M2, with mu = 2^mu_log2),
+ * then dX = dY W^T and dW = X^T dY from the FP8 copies the forward left
+ * in ws.
  *   dY [M,N] bf16; dX [M,K] bf16 or NULL to skip; dW [K,N] bf16 or NULL to skip.
  */
 fp8_status fp8_linear_bwd(const void* dY, int64_t M, int64_t K, int64_t N, int margin, int mu_log2,

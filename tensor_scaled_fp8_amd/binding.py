@@ -3,8 +3,8 @@ marshalling only. Torch supplies device memory and the current HIP stream;
 every step of the computation runs in the HIP kernels of libfp8lin.so.
 
 Names follow the C entry points: fp8_amax, fp8_scale, fp8_amax_scale,
-fp8_cast, fp8_gemm_nt, fp8_linear_fwd, fp8_linear_bwd. A scaling record
-(fp8_scale_t, 32 bytes) is an int32 tensor of 8 words on the device."""
+fp8_cast, fp8_gemm_nt, fp8_quantize, fp8_linear_fwd, fp8_linear_bwd. A scaling record
+(fp8_scale_t, 64 bytes) is an int32 tensor of 16 words on the device."""
 from __future__ import annotations
 
 import ctypes
@@ -15,7 +15,7 @@ import torch
 from . import _lib
 from ._lib import FP8_E4M3, FP8_E5M2, LinearWs, check, load
 
-SCALE_WORDS = 8          # sizeof(fp8_scale_t) / 4
+SCALE_WORDS = 16         # sizeof(fp8_scale_t) / 4
 FMT_CODES = {"e4m3": FP8_E4M3, "e5m2": FP8_E5M2, FP8_E4M3: FP8_E4M3, FP8_E5M2: FP8_E5M2}
 
 
@@ -43,7 +43,7 @@ def _dev(t: Optional[torch.Tensor], dtype, name: str) -> Optional[int]:
 
 
 def new_scale(count: int = 1, device="cuda") -> torch.Tensor:
-    """Zeroed scaling record(s): int32 [count, 8] (or [8] for count=1 via [0])."""
+    """Zeroed scaling record(s): int32 [count, 16]."""
     return torch.zeros((count, SCALE_WORDS), dtype=torch.int32, device=device)
 
 
@@ -96,6 +96,24 @@ def fp8_cast(x: torch.Tensor, fmt, s: torch.Tensor, out_row: Optional[torch.Tens
     check(load().fp8_cast(_dev(x, torch.bfloat16, "x"), rows, cols, _fmt(fmt), _dev(s, torch.int32, "s"),
                           _dev(out_row, torch.uint8, "out_row"), _dev(out_t, torch.uint8, "out_t"),
                           _stream(x)), "fp8_cast")
+    return out_row, out_t
+
+
+def fp8_quantize(x: torch.Tensor, fmt, s: torch.Tensor, margin: int = 0, mu_log2: int = 0,
+                 out_row: Optional[torch.Tensor] = None, out_t: Optional[torch.Tensor] = None,
+                 rowwise: bool = True, transposed: bool = True):
+    """amax + scale + cast (+ transpose) of a bf16 [rows, cols] matrix in one
+    call; returns (rowwise or None, transposed or None)."""
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D")
+    rows, cols = x.shape
+    if rowwise and out_row is None:
+        out_row = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    if transposed and out_t is None:
+        out_t = torch.empty((cols, rows), dtype=torch.uint8, device=x.device)
+    check(load().fp8_quantize(_dev(x, torch.bfloat16, "x"), rows, cols, _fmt(fmt), margin, mu_log2,
+                              _dev(s, torch.int32, "s"), _dev(out_row, torch.uint8, "out_row"),
+                              _dev(out_t, torch.uint8, "out_t"), _stream(x)), "fp8_quantize")
     return out_row, out_t
 
 

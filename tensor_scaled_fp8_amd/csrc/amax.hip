@@ -8,28 +8,31 @@
 // every finite value and NaN patterns above inf, so the integer max also
 // detects non-finite values. Two packed 16-bit maxima per dword (one VALU
 // op per two values), a wavefront max by cross-lane exchange, a block max
-// through LDS. Each block then merges into the record's reduction word
-// with a device-scope atomic max, but only when its value exceeds what the
-// word already holds: same-address atomics from thousands of blocks
-// serialise, and after the first few blocks almost none is needed. A
-// one-thread kernel on the same stream then publishes amax (and the scale)
-// and clears the reduction word for the next call; the launch boundary
-// orders it after every block's atomic.
+// through LDS. Blocks then merge with a device-scope atomic max, skipped
+// when the target word already holds at least as much (same-address
+// atomics from many blocks serialise). Two ways to finish:
+//  * amax_kernel (fp8_amax / fp8_amax_scale, self-contained): each block
+//    waits until its max is performed, then takes a ticket; device-scope
+//    atomics are performed at one coherence point, so the block with the
+//    last ticket sees every block's max, publishes amax (and the scale) and
+//    clears the reduction word and the ticket. No L2-writeback fence.
+//  * amax_gen_kernel (fp8_quantize): merges (gen << 16) | max into a 64-bit
+//    word, gen growing with every call so older maxima never win; nothing
+//    waits inside the kernel and the word is never cleared. The cast kernel
+//    that follows derives the scale from the word and publishes the record.
 #include "fp8lin_internal.h"
 
 namespace fp8lin {
 namespace {
 
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 8;         // 16-byte loads in flight per thread
-constexpr int kMaxBlocks = 1024;   // 4 blocks per CU on 256 CUs
+constexpr int kUnroll = 8;        // 16-byte loads in flight per thread
+constexpr int kMaxBlocks = 512;   // 2 blocks per CU on 256 CUs (one merge atomic each at most)
 
 __device__ inline u16x2 as_u16x2(uint32_t v) { return __builtin_bit_cast(u16x2, v); }
-__device__ inline uint32_t as_u32(u16x2 v) { return __builtin_bit_cast(uint32_t, v); }
 
 __device__ inline u16x2 vmax(u16x2 a, uint32_t w) {
   return __builtin_elementwise_max(a, as_u16x2(w & 0x7FFF7FFFu));
@@ -53,12 +56,12 @@ __device__ inline void write_scale(fp8_scale_t* s, uint32_t mag, bool fuse, int 
   s->flags = flags;
 }
 
-__global__ __launch_bounds__(kThreads) void amax_kernel(const u32x4* __restrict__ x, int64_t n_vec,
-                                                        int64_t per_block,
-                                                        const uint16_t* __restrict__ tail,
-                                                        int tail_n, fp8_scale_t* s) {
+// Block-wide max of |x| bits over this block's contiguous chunk (block-
+// contiguous chunks of whole kUnroll*256-vector steps; block 0 also takes
+// the < 8-element tail). The result is valid in thread 0.
+__device__ inline uint32_t block_max_bits(const u32x4* __restrict__ x, int64_t n_vec, int64_t per_block,
+                                          const uint16_t* __restrict__ tail, int tail_n) {
   u16x2 m = {0, 0};
-  // block-contiguous chunk, kUnroll * 256 consecutive 16-byte vectors per step
   const int64_t b0 = (int64_t)blockIdx.x * per_block;
   const int64_t b1 = b0 + per_block < n_vec ? b0 + per_block : n_vec;
   int64_t base = b0;
@@ -85,9 +88,8 @@ __global__ __launch_bounds__(kThreads) void amax_kernel(const u32x4* __restrict_
     m = vmax(m, (uint32_t)tail[threadIdx.x]);
   }
   uint32_t r = m.x > m.y ? m.x : m.y;
-  // wavefront max
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
+  for (int off = 32; off > 0; off >>= 1) {  // wavefront max
     uint32_t o = (uint32_t)__shfl_xor((int)r, off, 64);
     r = o > r ? o : r;
   }
@@ -95,21 +97,43 @@ __global__ __launch_bounds__(kThreads) void amax_kernel(const u32x4* __restrict_
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   if (lane == 0) wmax[wid] = r;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t b = wmax[0];
+  uint32_t b = wmax[0];
 #pragma unroll
-    for (int w = 1; w < kThreads / 64; ++w) b = wmax[w] > b ? wmax[w] : b;
+  for (int w = 1; w < kThreads / 64; ++w) b = wmax[w] > b ? wmax[w] : b;
+  return b;
+}
+
+__global__ __launch_bounds__(kThreads) void amax_kernel(const u32x4* __restrict__ x, int64_t n_vec,
+                                                        int64_t per_block,
+                                                        const uint16_t* __restrict__ tail,
+                                                        int tail_n, fp8_scale_t* s, int fuse, int fmt,
+                                                        int margin, int mu_log2) {
+  const uint32_t b = block_max_bits(x, n_vec, per_block, tail, tail_n);
+  if (threadIdx.x == 0) {
     const uint32_t seen = __hip_atomic_load(&s->reduce_bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (b > seen) atomicMax(&s->reduce_bits, b);
+    // the max must have been performed before this block's ticket is taken
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    const uint32_t ticket = atomicAdd(&s->reduce_ticket, 1u);
+    if (ticket == gridDim.x - 1) {
+      const uint32_t mag = atomicExch(&s->reduce_bits, 0u);
+      atomicExch(&s->reduce_ticket, 0u);
+      write_scale(s, mag, fuse != 0, fmt, margin, mu_log2);
+    }
   }
 }
 
-// Publishes the reduced amax (and, when fused, the scale) and clears the
-// reduction word. One thread; runs after amax_kernel on the same stream.
-__global__ void amax_finish_kernel(fp8_scale_t* s, int fuse, int fmt, int margin, int mu_log2) {
-  const uint32_t mag = atomicExch(&s->reduce_bits, 0u);
-  s->reduce_ticket = 0u;
-  write_scale(s, mag, fuse != 0, fmt, margin, mu_log2);
+__global__ __launch_bounds__(kThreads) void amax_gen_kernel(const u32x4* __restrict__ x, int64_t n_vec,
+                                                            int64_t per_block,
+                                                            const uint16_t* __restrict__ tail,
+                                                            int tail_n, fp8_scale_t* s, uint64_t gen) {
+  const uint32_t b = block_max_bits(x, n_vec, per_block, tail, tail_n);
+  if (threadIdx.x == 0) {
+    const unsigned long long v = ((unsigned long long)gen << 16) | b;
+    unsigned long long* word = (unsigned long long*)&s->gen_max;
+    const unsigned long long seen = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (v > seen) atomicMax(word, v);
+  }
 }
 
 __global__ void scale_kernel(fp8_scale_t* s, int fmt, int margin, int mu_log2) {
@@ -138,23 +162,39 @@ hipError_t launch_scale_reset(fp8_scale_t* s, int64_t count, hipStream_t st) {
   return hipGetLastError();
 }
 
+namespace {
+struct SweepGrid {
+  int64_t n_vec, per_block, blocks;
+  int tail_n;
+  const uint16_t* tail;
+};
+// enough blocks to fill the chip, each a contiguous chunk of whole steps
+SweepGrid sweep_grid(const void* x, int64_t n) {
+  SweepGrid g;
+  g.n_vec = n / 8;
+  g.tail_n = (int)(n - g.n_vec * 8);
+  g.tail = (const uint16_t*)x + g.n_vec * 8;
+  const int64_t step = (int64_t)kThreads * kUnroll;
+  int64_t blocks = (g.n_vec + step - 1) / step;
+  blocks = blocks < 1 ? 1 : (blocks > kMaxBlocks ? kMaxBlocks : blocks);
+  g.per_block = ((g.n_vec + blocks - 1) / blocks + step - 1) / step * step;
+  g.blocks = g.n_vec > 0 ? (g.n_vec + g.per_block - 1) / g.per_block : 1;
+  return g;
+}
+}  // namespace
+
 hipError_t launch_amax(const void* x, int64_t n, fp8_scale_t* s, bool fuse_scale, int fmt, int margin,
                        int mu_log2, hipStream_t st) {
-  const int64_t n_vec = n / 8;
-  const int tail_n = (int)(n - n_vec * 8);
-  const uint16_t* tail = (const uint16_t*)x + n_vec * 8;
-  // enough blocks to fill the chip, each a contiguous chunk of whole steps
-  const int64_t step = (int64_t)kThreads * kUnroll;
-  int64_t blocks = (n_vec + step - 1) / step;
-  blocks = blocks < 1 ? 1 : (blocks > kMaxBlocks ? kMaxBlocks : blocks);
-  const int64_t per_block = ((n_vec + blocks - 1) / blocks + step - 1) / step * step;
-  blocks = n_vec > 0 ? (n_vec + per_block - 1) / per_block : 1;
-  hipLaunchKernelGGL(amax_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, st, (const u32x4*)x, n_vec,
-                     per_block, tail, tail_n, s);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(amax_finish_kernel, dim3(1), dim3(1), 0, st, s, fuse_scale ? 1 : 0, fmt, margin,
-                     mu_log2);
+  const SweepGrid g = sweep_grid(x, n);
+  hipLaunchKernelGGL(amax_kernel, dim3((unsigned)g.blocks), dim3(kThreads), 0, st, (const u32x4*)x, g.n_vec,
+                     g.per_block, g.tail, g.tail_n, s, fuse_scale ? 1 : 0, fmt, margin, mu_log2);
+  return hipGetLastError();
+}
+
+hipError_t launch_amax_gen(const void* x, int64_t n, fp8_scale_t* s, uint64_t gen, hipStream_t st) {
+  const SweepGrid g = sweep_grid(x, n);
+  hipLaunchKernelGGL(amax_gen_kernel, dim3((unsigned)g.blocks), dim3(kThreads), 0, st, (const u32x4*)x,
+                     g.n_vec, g.per_block, g.tail, g.tail_n, s, gen);
   return hipGetLastError();
 }
 

@@ -2,9 +2,18 @@
 // launches on the caller's stream. No allocation, no host synchronisation.
 #include <string.h>
 
+#include <atomic>
+
 #include "fp8lin_internal.h"
 
 using namespace fp8lin;
+
+namespace fp8lin {
+uint64_t next_generation() {
+  static std::atomic<uint64_t> counter{1};
+  return counter.fetch_add(1, std::memory_order_relaxed) & ((uint64_t(1) << 48) - 1);
+}
+}  // namespace fp8lin
 
 namespace {
 
@@ -83,6 +92,22 @@ fp8_status fp8_cast(const void* x_bf16, int64_t rows, int64_t cols, fp8_fmt fmt,
   return hip_status(launch_cast(x_bf16, rows, cols, fmt, s_dev, out_rowwise, out_transposed, stream));
 }
 
+fp8_status fp8_quantize(const void* x_bf16, int64_t rows, int64_t cols, fp8_fmt fmt, int margin,
+                        int mu_log2, fp8_scale_t* s_dev, uint8_t* out_rowwise, uint8_t* out_transposed,
+                        hipStream_t stream) {
+  if (rows < 0 || cols < 0 || !fmt_ok(fmt) || !int_ok(margin) || !int_ok(mu_log2) || !s_dev ||
+      !aligned16(s_dev))
+    return FP8_ERR_INVALID;
+  if (rows % 16 || cols % 16 || rows >= kMaxDim || cols >= kMaxDim) return FP8_ERR_UNSUPPORTED;
+  if (rows > 0 && cols > 0) {
+    if (!x_bf16 || !aligned16(x_bf16)) return FP8_ERR_INVALID;
+    if (out_rowwise && !aligned16(out_rowwise)) return FP8_ERR_INVALID;
+    if (out_transposed && !aligned16(out_transposed)) return FP8_ERR_INVALID;
+  }
+  return hip_status(launch_quantize(x_bf16, rows, cols, fmt, margin, mu_log2, s_dev, out_rowwise,
+                                    out_transposed, next_generation(), stream));
+}
+
 fp8_status fp8_gemm_nt(const uint8_t* A, fp8_fmt fa, const fp8_scale_t* sa, const uint8_t* B,
                        fp8_fmt fb, const fp8_scale_t* sb, int64_t M, int64_t N, int64_t R,
                        void* C_bf16, hipStream_t stream) {
@@ -121,11 +146,12 @@ fp8_status fp8_linear_fwd(const void* X, const void* W, int64_t M, int64_t K, in
   if ((M * K > 0 && (!X || !aligned16(X))) || (K * N > 0 && (!W || !aligned16(W))) ||
       (M * N > 0 && (!Y || !aligned16(Y))))
     return FP8_ERR_INVALID;
-  hipError_t e;
-  if ((e = launch_amax(X, M * K, ws->sx, true, FP8_E4M3, margin, 0, stream)) != hipSuccess) return FP8_ERR_HIP;
-  if ((e = launch_amax(W, K * N, ws->sw, true, FP8_E4M3, margin, 0, stream)) != hipSuccess) return FP8_ERR_HIP;
-  if ((e = launch_cast(X, M, K, FP8_E4M3, ws->sx, ws->x8, ws->x8t, stream)) != hipSuccess) return FP8_ERR_HIP;
-  if ((e = launch_cast(W, K, N, FP8_E4M3, ws->sw, ws->w8, ws->w8t, stream)) != hipSuccess) return FP8_ERR_HIP;
+  if (launch_quantize(X, M, K, FP8_E4M3, margin, 0, ws->sx, ws->x8, ws->x8t, next_generation(), stream) !=
+      hipSuccess)
+    return FP8_ERR_HIP;
+  if (launch_quantize(W, K, N, FP8_E4M3, margin, 0, ws->sw, ws->w8, ws->w8t, next_generation(), stream) !=
+      hipSuccess)
+    return FP8_ERR_HIP;
   return hip_status(launch_gemm(ws->x8, FP8_E4M3, ws->sx, ws->w8t, FP8_E4M3, ws->sw, M, N, K, Y, stream));
 }
 
@@ -140,9 +166,8 @@ fp8_status fp8_linear_bwd(const void* dY, int64_t M, int64_t K, int64_t N, int m
   if ((M * N > 0 && (!dY || !aligned16(dY))) || (dX && !aligned16(dX)) || (dW && !aligned16(dW)))
     return FP8_ERR_INVALID;
   hipError_t e;
-  if ((e = launch_amax(dY, M * N, ws->sdy, true, FP8_E5M2, margin, mu_log2, stream)) != hipSuccess)
-    return FP8_ERR_HIP;
-  if ((e = launch_cast(dY, M, N, FP8_E5M2, ws->sdy, ws->dy8, ws->dy8t, stream)) != hipSuccess)
+  if ((e = launch_quantize(dY, M, N, FP8_E5M2, margin, mu_log2, ws->sdy, ws->dy8, ws->dy8t, next_generation(),
+                           stream)) != hipSuccess)
     return FP8_ERR_HIP;
   if (dX && (e = launch_gemm(ws->dy8, FP8_E5M2, ws->sdy, ws->w8, FP8_E4M3, ws->sw, M, K, N, dX, stream)) !=
                 hipSuccess)

@@ -76,19 +76,44 @@ __device__ inline void transpose4(const uint32_t in[4], uint32_t out[4]) {
   out[3] = __builtin_amdgcn_perm(b1, a1, 0x07060302u);
 }
 
-template <int FMT>
+// DERIVE = false: the scale comes from the record's published fields.
+// DERIVE = true (fp8_quantize): every block derives it from the record's
+// generation-tagged maximum, which the amax pass just merged, with the same
+// rule as fp8_scale; block 0 publishes the record's fields.
+template <int FMT, bool DERIVE>
 __global__ __launch_bounds__(kThreads) void cast_kernel(const uint16_t* __restrict__ x, int64_t rows,
-                                                        int64_t cols, int64_t tiles_c,
-                                                        const fp8_scale_t* __restrict__ s,
+                                                        int64_t cols, int64_t tiles_c, fp8_scale_t* s,
                                                         uint8_t* __restrict__ out_row,
-                                                        uint8_t* __restrict__ out_t) {
+                                                        uint8_t* __restrict__ out_t, int margin,
+                                                        int mu_log2) {
   __shared__ uint4 lds[kTile * kTile / 16];  // transposed tile: 128 rows of 128 bytes
   const int t = threadIdx.x;
   const int64_t tr = blockIdx.x / tiles_c, tc = blockIdx.x - (blockIdx.x / tiles_c) * tiles_c;
   const int64_t r0 = tr * kTile, c0 = tc * kTile;
   const int rg = t >> 4, cc = t & 15;
-  const float scale = s->scale;
-  const bool nonfinite = (s->flags & FP8_FLAG_NONFINITE) != 0u;
+  float scale;
+  bool nonfinite;
+  if constexpr (DERIVE) {
+    const unsigned long long word =
+        __hip_atomic_load((unsigned long long*)&s->gen_max, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t mag = (uint32_t)(word & 0xFFFFu);
+    uint32_t flags;
+    const int32_t b = bias_from_amax_bits(mag << 16, FMT, margin, mu_log2, &flags);
+    scale = pow2f(b);
+    nonfinite = (flags & FP8_FLAG_NONFINITE) != 0u;
+    if (blockIdx.x == 0 && t == 0) {
+      union { uint32_t u; float f; } a;
+      a.u = mag << 16;
+      s->amax = a.f;
+      s->bias = b;
+      s->scale = scale;
+      s->scale_inv = pow2f(-b);
+      s->flags = flags;
+    }
+  } else {
+    scale = s->scale;
+    nonfinite = (s->flags & FP8_FLAG_NONFINITE) != 0u;
+  }
   const int64_t rr = r0 + 8 * rg, cx = c0 + 8 * cc;
   const bool ok = rr < rows && cx < cols;  // rows, cols are multiples of 16
 
@@ -146,20 +171,38 @@ __global__ __launch_bounds__(kThreads) void cast_kernel(const uint16_t* __restri
   }
 }
 
+template <bool DERIVE>
+hipError_t launch_cast_t(const void* x, int64_t rows, int64_t cols, int fmt, fp8_scale_t* s,
+                         uint8_t* out_row, uint8_t* out_t, int margin, int mu_log2, hipStream_t st) {
+  int64_t tiles_r = (rows + kTile - 1) / kTile, tiles_c = (cols + kTile - 1) / kTile;
+  if (tiles_r * tiles_c == 0) tiles_r = tiles_c = 1;  // empty: one block that reads nothing (publishes)
+  const dim3 grid((unsigned)(tiles_r * tiles_c));
+  if (fmt == FP8_E4M3)
+    hipLaunchKernelGGL((cast_kernel<FP8_E4M3, DERIVE>), grid, dim3(kThreads), 0, st, (const uint16_t*)x,
+                       rows, cols, tiles_c, s, out_row, out_t, margin, mu_log2);
+  else
+    hipLaunchKernelGGL((cast_kernel<FP8_E5M2, DERIVE>), grid, dim3(kThreads), 0, st, (const uint16_t*)x,
+                       rows, cols, tiles_c, s, out_row, out_t, margin, mu_log2);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_cast(const void* x, int64_t rows, int64_t cols, int fmt, const fp8_scale_t* s,
                        uint8_t* out_row, uint8_t* out_t, hipStream_t st) {
   if (rows == 0 || cols == 0 || (!out_row && !out_t)) return hipSuccess;
-  const int64_t tiles_r = (rows + kTile - 1) / kTile, tiles_c = (cols + kTile - 1) / kTile;
-  const dim3 grid((unsigned)(tiles_r * tiles_c));
-  if (fmt == FP8_E4M3)
-    hipLaunchKernelGGL(cast_kernel<FP8_E4M3>, grid, dim3(kThreads), 0, st, (const uint16_t*)x, rows,
-                       cols, tiles_c, s, out_row, out_t);
-  else
-    hipLaunchKernelGGL(cast_kernel<FP8_E5M2>, grid, dim3(kThreads), 0, st, (const uint16_t*)x, rows,
-                       cols, tiles_c, s, out_row, out_t);
-  return hipGetLastError();
+  return launch_cast_t<false>(x, rows, cols, fmt, const_cast<fp8_scale_t*>(s), out_row, out_t, 0, 0, st);
+}
+
+hipError_t launch_quantize(const void* x, int64_t rows, int64_t cols, int fmt, int margin, int mu_log2,
+                           fp8_scale_t* s, uint8_t* out_row, uint8_t* out_t, uint64_t gen, hipStream_t st) {
+  hipError_t e = launch_amax_gen(x, rows * cols, s, gen, st);
+  if (e != hipSuccess) return e;
+  if (rows == 0 || cols == 0 || (!out_row && !out_t)) {
+    // nothing to cast: one block with no rows still publishes the record
+    return launch_cast_t<true>(x, 0, 0, fmt, s, nullptr, nullptr, margin, mu_log2, st);
+  }
+  return launch_cast_t<true>(x, rows, cols, fmt, s, out_row, out_t, margin, mu_log2, st);
 }
 
 }  // namespace fp8lin

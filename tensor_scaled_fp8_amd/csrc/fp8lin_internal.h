@@ -67,6 +67,13 @@ hipError_t launch_amax(const void* x, int64_t n, fp8_scale_t* s, bool fuse_scale
 hipError_t launch_scale(fp8_scale_t* s, int fmt, int margin, int mu_log2, hipStream_t st);
 hipError_t launch_cast(const void* x, int64_t rows, int64_t cols, int fmt, const fp8_scale_t* s,
                        uint8_t* out_row, uint8_t* out_t, hipStream_t st);
+hipError_t launch_amax_gen(const void* x, int64_t n, fp8_scale_t* s, uint64_t gen, hipStream_t st);
+// amax pass + cast that derives the scale (fp8_quantize); gen: a number
+// larger than any earlier call's (see next_generation)
+hipError_t launch_quantize(const void* x, int64_t rows, int64_t cols, int fmt, int margin, int mu_log2,
+                           fp8_scale_t* s, uint8_t* out_row, uint8_t* out_t, uint64_t gen, hipStream_t st);
+// process-wide increasing call number for fp8_quantize (48 bits used)
+uint64_t next_generation();
 hipError_t launch_gemm(const uint8_t* A, int fa, const fp8_scale_t* sa, const uint8_t* B, int fb,
                        const fp8_scale_t* sb, int64_t M, int64_t N, int64_t R, void* C,
                        hipStream_t st);

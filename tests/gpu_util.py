@@ -24,7 +24,7 @@ def u8(t: torch.Tensor) -> np.ndarray:
 
 def scale_record(bias: int, flags: int = 0, amax: float = 1.0) -> torch.Tensor:
     """A record with the given bias (scale = 2^bias), built on the host."""
-    raw = struct.pack("<fiffIIII", amax, bias, 2.0 ** bias, 2.0 ** -bias, flags, 0, 0, 0)
+    raw = struct.pack("<fiffIIII", amax, bias, 2.0 ** bias, 2.0 ** -bias, flags, 0, 0, 0) + bytes(32)
     return torch.from_numpy(np.frombuffer(raw, dtype=np.int32).copy()).cuda()
 
 

@@ -31,7 +31,7 @@ def test_header_functions_all_exported():
     for n in names:
         assert hasattr(lib, n), n
         assert n in _lib.SIGNATURES, f"binding lacks {n}"
-    assert lib.fp8_abi_version() == 1
+    assert lib.fp8_abi_version() == 2
 
 
 def test_status_strings():
@@ -78,6 +78,12 @@ def test_argument_validation_without_launch():
     assert lib.fp8_scale(0, 5000, 0, _vp(ok), None) == INV
     assert lib.fp8_amax_scale(_vp(ok), 8, 0, 0, -2000, _vp(ok), None) == INV
     assert lib.fp8_scale_reset(_vp(ok + 8), 1, None) == INV
+    q = lib.fp8_quantize
+    assert q(_vp(ok), 32, 40, 0, 0, 0, _vp(ok), _vp(ok), None, None) == UNS
+    assert q(_vp(ok), 32, 32, 2, 0, 0, _vp(ok), _vp(ok), None, None) == INV
+    assert q(_vp(ok), 32, 32, 0, 0, 9999, _vp(ok), _vp(ok), None, None) == INV
+    assert q(None, 32, 32, 0, 0, 0, _vp(ok), _vp(ok), None, None) == INV
+    assert q(_vp(ok), 32, 32, 1, 0, 0, None, _vp(ok), None, None) == INV
     # cast: dims must be multiples of 16
     assert lib.fp8_cast(_vp(ok), 17, 32, 0, _vp(ok), _vp(ok), None, None) == UNS
     assert lib.fp8_cast(_vp(ok), 32, 40, 1, _vp(ok), _vp(ok), None, None) == UNS

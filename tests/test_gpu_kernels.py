@@ -283,3 +283,63 @@ def test_autograd_linear_module():
     ref = x.detach().float() @ lin.weight.detach().float()
     rel = (y.float() - ref).norm() / ref.norm()
     assert rel < 0.08
+
+
+# ---------------------------------------------------------------- a1+a2+a3 fused
+@pytest.mark.parametrize("shape", [(16, 16), (144, 272), (528, 1040), (2064, 784)])
+@pytest.mark.parametrize("fmt_id,margin,mu", [(0, 0, 0), (1, 1, -2), (1, 0, 3), (0, 2, 0)])
+def test_quantize_matches_oracle(shape, fmt_id, margin, mu):
+    bits = draw_normal_bf16(shape[0] * 13 + shape[1] + fmt_id, shape, 0.02 if fmt_id == 0 else 1e-5)
+    x = to_dev_bf16(bits)
+    s = tsf.new_scale(1)[0]
+    rw, tr = tsf.fp8_quantize(x, NAME[fmt_id], s, margin, mu)
+    _check_record(tsf.read_scale(s), bits, fmt_id, margin, mu)
+    rec = oracle.scale_record(bits, FMT[fmt_id], margin, mu)
+    q, qt = oracle.cast(bits, FMT[fmt_id], rec["bias"])
+    assert np.array_equal(u8(rw), q) and np.array_equal(u8(tr), qt)
+
+
+def test_quantize_special_tensors_and_outputs():
+    n = 256
+    base = draw_normal_bf16(21, (n, n), 1.0)
+    cases = {"zeros": np.zeros((n, n), np.uint16), "nan": base.copy(), "inf": base.copy(),
+             "tiny": np.full((n, n), 0x0001, np.uint16)}
+    cases["nan"][3, 5] = 0xFFC1
+    cases["inf"][200, 7] = 0x7F80
+    for name, bits in cases.items():
+        for fmt_id in (0, 1):
+            s = tsf.new_scale(1)[0]
+            rw, tr = tsf.fp8_quantize(to_dev_bf16(bits), NAME[fmt_id], s)
+            _check_record(tsf.read_scale(s), bits, fmt_id, 0, 0)
+            rec = oracle.scale_record(bits, FMT[fmt_id])
+            q, qt = oracle.cast(bits, FMT[fmt_id], rec["bias"])
+            assert np.array_equal(u8(rw), q) and np.array_equal(u8(tr), qt), name
+    # single-output and no-output forms still publish the record
+    s = tsf.new_scale(1)[0]
+    rw, none = tsf.fp8_quantize(to_dev_bf16(base), "e4m3", s, transposed=False)
+    assert none is None
+    _check_record(tsf.read_scale(s), base, 0, 0, 0)
+    s = tsf.new_scale(1)[0]
+    tsf.fp8_quantize(to_dev_bf16(base), "e5m2", s, rowwise=False, transposed=False)
+    _check_record(tsf.read_scale(s), base, 1, 0, 0)
+    s = tsf.new_scale(1)[0]
+    tsf.fp8_quantize(torch.empty((0, 64), dtype=torch.bfloat16, device="cuda"), "e4m3", s)
+    r = tsf.read_scale(s)
+    assert r["amax"] == 0.0 and r["flags"] == tsf.FLAG_ZERO and r["bias"] == 0
+
+
+def test_quantize_repeated_calls_shrinking_amax():
+    """The generation-tagged running max must not keep an earlier call's
+    larger maximum; interleaving with the standalone amax path on the same
+    record keeps both correct."""
+    s = tsf.new_scale(1)[0]
+    for k, sigma in enumerate((100.0, 1.0, 1e-3, 50.0, 1e-6, 2.0)):
+        bits = draw_normal_bf16(300 + k, (128, 256), sigma)
+        x = to_dev_bf16(bits)
+        rw, _ = tsf.fp8_quantize(x, "e4m3", s, transposed=False)
+        _check_record(tsf.read_scale(s), bits, 0, 0, 0)
+        rec = oracle.scale_record(bits, E4M3)
+        assert np.array_equal(u8(rw), oracle.cast(bits, E4M3, rec["bias"])[0])
+        if k % 2:
+            tsf.fp8_amax_scale(x, "e5m2", s, 1, 0)
+            _check_record(tsf.read_scale(s), bits, 1, 1, 0)
