@@ -26,8 +26,7 @@
 //  * A direct-to-LDS load writes lane l's 16 bytes at slot l of a 1 KB LDS
 //    block (16 rows x 64 bytes), so the bank swizzle is applied on the
 //    source side: the lane for LDS chunk p of row r fetches global chunk
-//    p ^ swz(r). Fragment reads of 8 or 16 consecutive rows then hit
-//    distinct banks.
+//    p ^ swz(r). Fragment reads then hit distinct banks.
 //  * The MFMA is fed B as its first operand and A as its second, so it
 //    produces C^T blocks: each lane then holds 4 runs of 4 consecutive
 //    output columns of one row. The epilogue scales by 2^-(ba+bb), packs
@@ -66,10 +65,13 @@ typedef LDS_AS uint8_t lds_u8;
 typedef LDS_AS u32x4 lds_u32x4;
 typedef LDS_AS u32x2 lds_u32x2;
 
-// 16-byte chunk swizzle of a 64-byte LDS row: 8 consecutive rows (32 banks)
-// and 16 consecutive rows (64 banks) read at one logical chunk land on
-// distinct banks.
-__device__ inline int swz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+// 16-byte chunk swizzle of a 64-byte LDS row (four rows share one 256-byte
+// bank line). A fragment read has each lane take chunk 2g or 2g+1 of row
+// (lane & 31), g = lane >> 5. With swz = (row >> 2) & 3, the 16 rows of a
+// 16-lane group at one chunk land on 16 distinct 16-byte bank groups, and
+// so do 8 rows x both halves (chunks c, c+2) when lanes l and l+32 are
+// served together: swz(r) ^ swz(r+4) always has bit 0 set.
+__device__ inline int swz(int row) { return (row >> 2) & 3; }
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
 // vmcnt low bits [3:0], high bits [15:14]; expcnt 7 and lgkmcnt 15 = no wait)
@@ -256,7 +258,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
   // steady state: every stage touched is full, stage kt+4 exists. Hard
   // scheduling fences keep the order: first-half MFMAs | wait + barrier |
   // loads of stage kt+4 and fragment reads of stage kt+1 interleaved with
-  // the second-half MFMAs (one MFMA, one load, two reads per slot).
+  // the second-half MFMAs (two reads, one load, one MFMA per slot).
   auto step_main = [&](auto J_, int kt) {
     constexpr int J = decltype(J_)::value;
     Frags& cur = fr[J & 1];
@@ -269,11 +271,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
     issue_full(slot(J_), kt + 4);
     read_stage(slot(std::integral_constant<int, J + 1>{}), nxt);
     mfma_rows(cur, 2);
+    // reads first in each slot, so the last fragment reads are in flight
+    // before the last MFMA of the stage is issued
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read (direct-to-LDS)
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read (direct-to-LDS)
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
     }
     __builtin_amdgcn_sched_barrier(0);
   };
