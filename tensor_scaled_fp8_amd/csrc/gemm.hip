@@ -14,19 +14,24 @@
 //  * 256 x 256 output tile per 256-thread block (4 waves, 2 x 2), each wave
 //    128 x 128 = 4 x 4 MFMA blocks (256 FP32 accumulators per lane, held in
 //    the accumulation registers).
-//  * Operands stream through a 4-slot LDS ring of k = 64-byte stages
-//    (32 KB each: 256 rows of A and of B). Global memory is copied straight
-//    into LDS by 16-byte direct-to-LDS loads (no register staging), issued
-//    four stages ahead of use. With one wave per SIMD nothing else hides
-//    the non-MFMA work, so each stage is software-pipelined: the first half
-//    of its 16 MFMAs runs on fragments already in registers; then the next
-//    stage's loads are awaited (in-order vmcnt), one barrier frees the
-//    current slot, the loads of stage+4 are issued into it and the next
-//    stage's fragments are read, all under the second half of the MFMAs.
-//  * A direct-to-LDS load writes lane l's 16 bytes at slot l of a 1 KB LDS
-//    block (16 rows x 64 bytes), so the bank swizzle is applied on the
-//    source side: the lane for LDS chunk p of row r fetches global chunk
-//    p ^ swz(r). Fragment reads then hit distinct banks.
+//  * Operands stream through two 64 KB LDS buffers, each holding one stage
+//    of k = 128 bytes (256 rows of A and of B). 128 bytes is one cache line
+//    per row: a 16-byte-per-lane load then covers 8 whole lines, which the
+//    load path handles markedly faster than 16 half lines. Global memory is
+//    copied straight into LDS by buffer loads with the LDS-write form (no
+//    register staging); a stage is loaded while the previous one is
+//    multiplied.
+//  * Each stage is two MFMA steps of k = 64 (16 MFMAs per wave each). With
+//    one wave per SIMD nothing else hides the non-MFMA work, so the steps
+//    are software-pipelined: fragments of the next step are read from LDS
+//    into a second register set under the current step's MFMAs. One
+//    barrier per stage: at the second step of stage s, stage s+1 is awaited,
+//    and the loads of stage s+2 go into stage s's buffer, whose fragments
+//    every wave has read by then.
+//  * A load writes lane l's 16 bytes at slot l of a 1 KB LDS block (8 rows
+//    x 128 bytes), so the bank swizzle is applied on the source side: the
+//    lane for LDS chunk p of row r fetches global chunk p ^ swz(r).
+//    Fragment reads then hit distinct banks.
 //  * The MFMA is fed B as its first operand and A as its second, so it
 //    produces C^T blocks: each lane then holds 4 runs of 4 consecutive
 //    output columns of one row. The epilogue scales by 2^-(ba+bb), packs
@@ -51,12 +56,13 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kBM = 256, kBN = 256, kBK = 64;   // tile rows, tile cols, k-bytes per stage
+constexpr int kBM = 256, kBN = 256;
+constexpr int kBK = 128;                         // k-bytes per stage (one cache line per row)
 constexpr int kThreads = 256;
 constexpr int kGroupM = 8;                       // tile rows per raster group
-constexpr int kStages = 4;                       // LDS ring slots (all four hold stages in flight)
-constexpr int kStageBytes = (kBM + kBN) * kBK;   // 32 KB
-constexpr int kLoadsPerStage = 8;                // direct-to-LDS loads per thread per stage
+constexpr int kOpBytes = kBM * kBK;              // 32 KB: the A (or B) part of a stage
+constexpr int kStageBytes = 2 * kOpBytes;        // 64 KB; two stage buffers
+constexpr int kRsrcWord3 = 0x00020000;           // buffer resource word 3 for raw byte loads (gfx9 family)
 
 #define LDS_AS __attribute__((address_space(3)))
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -65,13 +71,12 @@ typedef LDS_AS uint8_t lds_u8;
 typedef LDS_AS u32x4 lds_u32x4;
 typedef LDS_AS u32x2 lds_u32x2;
 
-// 16-byte chunk swizzle of a 64-byte LDS row (four rows share one 256-byte
-// bank line). A fragment read has each lane take chunk 2g or 2g+1 of row
-// (lane & 31), g = lane >> 5. With swz = (row >> 2) & 3, the 16 rows of a
-// 16-lane group at one chunk land on 16 distinct 16-byte bank groups, and
-// so do 8 rows x both halves (chunks c, c+2) when lanes l and l+32 are
-// served together: swz(r) ^ swz(r+4) always has bit 0 set.
-__device__ inline int swz(int row) { return (row >> 2) & 3; }
+// 16-byte chunk swizzle of a 128-byte LDS row (two rows share one 256-byte
+// bank line). A fragment read has each lane take one chunk of row
+// (lane & 31); with swz = (row >> 1) & 7, the 16 rows of a 16-lane group at
+// one logical chunk land on 16 distinct 16-byte bank groups (row & 1 picks
+// the half of the bank line, the swizzled chunk the group within it).
+__device__ inline int swz(int row) { return (row >> 1) & 7; }
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
 // vmcnt low bits [3:0], high bits [15:14]; expcnt 7 and lgkmcnt 15 = no wait)
@@ -81,12 +86,21 @@ __device__ inline void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-__device__ inline void wait_loads_after(int n_after_full) {
-  // stages issued after the one to be consumed, each kLoadsPerStage loads
-  if (n_after_full >= 3) wait_vmcnt<3 * kLoadsPerStage>();
-  else if (n_after_full == 2) wait_vmcnt<2 * kLoadsPerStage>();
-  else if (n_after_full == 1) wait_vmcnt<kLoadsPerStage>();
-  else wait_vmcnt<0>();
+// calls f(integral_constant<int, 0>) ... f(integral_constant<int, N-1>) in order
+template <int N, int I = 0, typename F>
+__device__ inline void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(f);
+  }
+}
+
+__device__ inline void block_sync() {
+  // workgroup barrier only (no wait for this wave's LDS accesses); the empty
+  // asm keeps the compiler from moving memory accesses across it
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 __device__ inline void block_sync_lds() {
@@ -103,22 +117,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ B, const fp8_scale_t* __restrict__ sa,
     const fp8_scale_t* __restrict__ sb, int M, int N, int R, uint16_t* __restrict__ C, int tiles_m,
     int tiles_n) {
-  // The ring's four slots are four separate LDS objects, always addressed
-  // with a compile-time slot index, so the compiler can tell the slot being
-  // read from the slots with loads in flight and does not wait for those.
-  __shared__ uint4 slot0[kStageBytes / 16], slot1[kStageBytes / 16], slot2[kStageBytes / 16],
-      slot3[kStageBytes / 16];
+  // The two stage buffers are separate LDS objects, always addressed with a
+  // compile-time index, so the compiler can tell the buffer being read from
+  // the one with loads in flight and does not wait for those.
+  __shared__ uint4 slot0[kStageBytes / 16], slot1[kStageBytes / 16];
   auto slot = [&](auto J_) -> lds_u8* {
-    constexpr int J = decltype(J_)::value % kStages;
-    if constexpr (J == 0) return (lds_u8*)slot0;
-    else if constexpr (J == 1) return (lds_u8*)slot1;
-    else if constexpr (J == 2) return (lds_u8*)slot2;
-    else return (lds_u8*)slot3;
+    if constexpr ((decltype(J_)::value & 1) == 0) return (lds_u8*)slot0;
+    else return (lds_u8*)slot1;
   };
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
-  using S2 = std::integral_constant<int, 2>;
-  using S3 = std::integral_constant<int, 3>;
 
   // ---- tile selection: XCD-contiguous ranges, grouped raster inside ----
   const int nblocks = tiles_m * tiles_n;
@@ -137,32 +145,37 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);  // wave index, scalar
   const int wm = w >> 1, wn = w & 1;
 
-  // ---- direct-to-LDS loads: wave w fills 1 KB blocks 4w..4w+3 of the A and
-  // B halves of a stage; lane l of block b writes row 16b + l/4, LDS chunk
-  // l%4. Operands are below 4 GiB, so per-lane offsets are 32-bit.
-  uint32_t offa[4], offb[4];
-  int kc[4];
+  // ---- loads: wave w fills 1 KB blocks 8w..8w+7 of the A and B parts of a
+  // stage; lane l of block b writes row 8b + l/8, LDS chunk l%8, which holds
+  // global chunk (l%8) ^ swz(row). Operands are below 4 GiB, so per-lane
+  // offsets are 32-bit; the stage's k offset is a scalar.
+  uint32_t offa[8], offb[8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = 16 * (4 * w + i) + (lane >> 2);
-    const int c = (lane & 3) ^ swz(row);
-    kc[i] = 16 * c;
-    offa[i] = (uint32_t)min(m0 + row, M - 1) * (uint32_t)R + kc[i];
-    offb[i] = (uint32_t)min(n0 + row, N - 1) * (uint32_t)R + kc[i];
+  for (int i = 0; i < 8; ++i) {
+    const int row = 8 * (8 * w + i) + (lane >> 3);
+    const int kc = 16 * ((lane & 7) ^ swz(row));
+    offa[i] = (uint32_t)min(m0 + row, M - 1) * (uint32_t)R + kc;
+    offb[i] = (uint32_t)min(n0 + row, N - 1) * (uint32_t)R + kc;
   }
-  const int nk = (R + kBK - 1) / kBK;      // k-stages
-  const int nfull = R / kBK;               // full k-stages (all but a partial last one)
+  const int nk = (R + kBK - 1) / kBK;      // stages
+  const int nfull = R / kBK;               // full stages (all but a partial last one)
 
-  // loads of one full stage: 4 of A, 4 of B per thread
+  // Buffer resources (base + byte count of each operand): being buffer (not
+  // flat) loads, they leave the compiler's count of outstanding LDS reads
+  // exact, so each MFMA waits only for its own fragments.
+  const __amdgpu_buffer_rsrc_t rsa =
+      __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, (int)((uint32_t)M * (uint32_t)R), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rsb =
+      __builtin_amdgcn_make_buffer_rsrc((void*)B, (short)0, (int)((uint32_t)N * (uint32_t)R), kRsrcWord3);
+  // the 16 loads (8 of A, 8 of B) of one full stage
   auto issue_full = [&](lds_u8* sl, int stage) {
-    const uint8_t* a0 = A + stage * kBK;  // wave-uniform bases; per-lane offsets
-    const uint8_t* b0 = B + stage * kBK;
-    lds_u8* sbase = sl + (4 * w) * 1024;
+    const int koff = stage * kBK;  // wave-uniform
+    lds_u8* sa_ = sl + (8 * w) * 1024;
+    lds_u8* sb_ = sl + kOpBytes + (8 * w) * 1024;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      __builtin_amdgcn_global_load_lds((const void*)(a0 + offa[i]), (LDS_AS void*)(sbase + i * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(b0 + offb[i]), (LDS_AS void*)(sbase + kBM * kBK + i * 1024),
-                                       16, 0, 0);
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (LDS_AS void*)(sa_ + i * 1024), 16, (int)offa[i], koff, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (LDS_AS void*)(sb_ + i * 1024), 16, (int)offb[i], koff, 0, 0);
     }
   };
   // any stage, including a partial last one (k past R zero-filled)
@@ -172,16 +185,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
       return;
     }
     const int k0 = stage * kBK;
-    const uint8_t* a0 = A + k0;
-    const uint8_t* b0 = B + k0;
-    lds_u8* sbase = sl + (4 * w) * 1024;
+    lds_u8* sa_ = sl + (8 * w) * 1024;
+    lds_u8* sb_ = sl + kOpBytes + (8 * w) * 1024;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      lds_u8* da = sbase + i * 1024;
-      lds_u8* db = sbase + kBM * kBK + i * 1024;
-      if (k0 + kc[i] < R) {
-        __builtin_amdgcn_global_load_lds((const void*)(a0 + offa[i]), (LDS_AS void*)da, 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const void*)(b0 + offb[i]), (LDS_AS void*)db, 16, 0, 0);
+    for (int i = 0; i < 8; ++i) {
+      const int row = 8 * (8 * w + i) + (lane >> 3);
+      const int kc = 16 * ((lane & 7) ^ swz(row));
+      lds_u8* da = sa_ + i * 1024;
+      lds_u8* db = sb_ + i * 1024;
+      if (k0 + kc < R) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (LDS_AS void*)da, 16, (int)offa[i], k0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (LDS_AS void*)db, 16, (int)offb[i], k0, 0, 0);
       } else {
         *(lds_u32x4*)(da + 16 * lane) = (u32x4){0, 0, 0, 0};
         *(lds_u32x4*)(db + 16 * lane) = (u32x4){0, 0, 0, 0};
@@ -189,31 +203,35 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
     }
   };
 
-  // ---- fragment reads: lane -> row (lane & 31), logical chunks 2g, 2g+1 ----
-  // swz() of every fragment row equals swz(lane & 31) (fragment rows start at
-  // multiples of 32), so two per-lane offsets plus compile-time immediates
-  // address every fragment of every slot.
+  // ---- fragment reads: lane -> row (lane & 31); step h (0, 1) of a stage
+  // takes logical chunks 4h + 2g and 4h + 2g + 1, g = lane >> 5. swz() of
+  // every fragment row equals swz(lane & 31) (fragment rows start at
+  // multiples of 32), so four per-lane offsets plus compile-time immediates
+  // address every fragment of both buffers.
   const int frow = lane & 31, g = lane >> 5;
   const int fsw = swz(frow);
-  const int off_lo = frow * kBK + (((2 * g) ^ fsw) << 4);
-  const int off_hi = frow * kBK + (((2 * g + 1) ^ fsw) << 4);
-  const int a_row0 = 128 * wm * kBK, b_row0 = kBM * kBK + 128 * wn * kBK;  // wave-uniform
+  int foff[2][2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) foff[h][j] = frow * kBK + (((4 * h + 2 * g + j) ^ fsw) << 4);
+  const int a_row0 = 128 * wm * kBK, b_row0 = kOpBytes + 128 * wn * kBK;  // wave-uniform
   struct Frags {
     v8i a[4], b[4];
   };
-  auto read_frag = [&](const lds_u8* p) -> v8i {
-    const u32x4 lo = *(const lds_u32x4*)(p + off_lo);
-    const u32x4 hi = *(const lds_u32x4*)(p + off_hi);
+  auto read_frag = [&](const lds_u8* p, int h) -> v8i {
+    const u32x4 lo = *(const lds_u32x4*)(p + foff[h][0]);
+    const u32x4 hi = *(const lds_u32x4*)(p + foff[h][1]);
     v8i v;
     v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
     v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
     return v;
   };
-  auto read_stage = [&](const lds_u8* sl, Frags& f) {
+  auto read_step = [&](const lds_u8* sl, int h, Frags& f) {
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni) f.b[ni] = read_frag(sl + b_row0 + 32 * ni * kBK);
+    for (int mi = 0; mi < 4; ++mi) f.a[mi] = read_frag(sl + a_row0 + 32 * mi * kBK, h);
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi) f.a[mi] = read_frag(sl + a_row0 + 32 * mi * kBK);
+    for (int ni = 0; ni < 4; ++ni) f.b[ni] = read_frag(sl + b_row0 + 32 * ni * kBK, h);
   };
 
   v16f acc[4][4];
@@ -224,96 +242,96 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.0f;
 
-  auto mfma_rows = [&](const Frags& f, int mlo) {
+  auto mfma_all = [&](const Frags& f) {
 #pragma unroll
-    for (int mi = mlo; mi < mlo + 2; ++mi)
+    for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
       for (int ni = 0; ni < 4; ++ni)
         acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[ni], f.a[mi], acc[mi][ni], FB, FA,
                                                                        0, 0, 0, 0);
   };
-  // wait until stage `st` has landed when stages up to `newest` are issued;
-  // the count of younger loads is exact only if they are all full stages
-  auto wait_for_stage = [&](int st, int newest) {
-    const bool full = newest < nfull;
-    wait_loads_after(full ? newest - st : 0);
-  };
 
-  // Software pipeline over k-stages. On entry to stage kt its fragments are
-  // in registers (fr[kt & 1]). The first half of its MFMAs runs, then:
-  // stage kt+1's loads are awaited, one barrier (every wave has finished
-  // reading slot kt), the loads of stage kt+4 go into that slot, and stage
-  // kt+1's fragments are read into the other register set while the second
-  // half of stage kt's MFMAs runs.
+  // Software pipeline. Stage s lives in buffer s % 2; its two MFMA steps use
+  // fr[0] (k-half 0) and fr[1] (k-half 1). On entry to stage s, fr[0] holds
+  // its first half and stage s+1's loads are in flight.
+  //  step 2s:   read k-half 1 of stage s into fr[1]; MFMAs on fr[0].
+  //  step 2s+1: wait for stage s+1 (own loads by vmcnt, everyone's by the
+  //             barrier, which also follows every wave's reads of buffer
+  //             s % 2); issue stage s+2 into buffer s % 2; read k-half 0 of
+  //             stage s+1 into fr[0]; MFMAs on fr[1].
   Frags fr[2];
   if (nk > 0) issue_any(slot(S0{}), 0);
   if (nk > 1) issue_any(slot(S1{}), 1);
-  if (nk > 2) issue_any(slot(S2{}), 2);
-  if (nk > 3) issue_any(slot(S3{}), 3);
   if (nk > 0) {
-    wait_for_stage(0, min(3, nk - 1));
+    if (nk > 1) {
+      if (nfull > 1) wait_vmcnt<16>();  // full stage 1 (16 loads) may stay in flight
+      else wait_vmcnt<0>();                      // partial stage 1: count not exact
+    } else {
+      wait_vmcnt<0>();
+    }
     block_sync_lds();
-    read_stage(slot(S0{}), fr[0]);
+    read_step(slot(S0{}), 0, fr[0]);
   }
-  // steady state: every stage touched is full, stage kt+4 exists. Hard
-  // scheduling fences keep the order: first-half MFMAs | wait + barrier |
-  // loads of stage kt+4 and fragment reads of stage kt+1 interleaved with
-  // the second-half MFMAs (two reads, one load, one MFMA per slot).
-  auto step_main = [&](auto J_, int kt) {
+  // steady state: stages s+1 and s+2 are full. Hard scheduling fences keep
+  // the order; the group hints interleave reads / loads with the MFMAs.
+  auto stage_main = [&](auto J_, int s) {
     constexpr int J = decltype(J_)::value;
-    Frags& cur = fr[J & 1];
-    Frags& nxt = fr[(J + 1) & 1];
-    mfma_rows(cur, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    wait_vmcnt<2 * kLoadsPerStage>();  // stage kt+1 landed (kt+2, kt+3 may be in flight)
-    block_sync_lds();
-    __builtin_amdgcn_sched_barrier(0);
-    issue_full(slot(J_), kt + 4);
-    read_stage(slot(std::integral_constant<int, J + 1>{}), nxt);
-    mfma_rows(cur, 2);
-    // reads first in each slot, so the last fragment reads are in flight
-    // before the last MFMA of the stage is issued
+    read_step(slot(J_), 1, fr[1]);
+    mfma_all(fr[0]);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read (direct-to-LDS)
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
     }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<0>();   // stage s+1 landed (the only loads in flight)
+    block_sync_lds();  // everyone's loads landed, everyone's reads of buffer J done
+    __builtin_amdgcn_sched_barrier(0);
+    issue_full(slot(J_), s + 2);
+    read_step(slot(std::integral_constant<int, J + 1>{}), 0, fr[0]);
+    mfma_all(fr[1]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
+      __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);  // buffer load to LDS
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     __builtin_amdgcn_sched_barrier(0);
   };
-  // general step (tail): bounds on every stage
-  auto step_any = [&](auto J_, int kt) {
+  // general stage (tail): bounds on every stage; zero-filled parts of a
+  // partial stage are LDS stores, made visible by the next barrier
+  // (block_sync_lds waits for this wave's LDS accesses first)
+  auto stage_any = [&](auto J_, int s) {
     constexpr int J = decltype(J_)::value;
-    Frags& cur = fr[J & 1];
-    Frags& nxt = fr[(J + 1) & 1];
-    mfma_rows(cur, 0);
-    if (kt + 1 < nk) {
-      wait_for_stage(kt + 1, min(kt + 3, nk - 1));
+    read_step(slot(J_), 1, fr[1]);
+    mfma_all(fr[0]);
+    if (s + 1 < nk) {
+      wait_vmcnt<0>();
       block_sync_lds();
-      if (kt + 4 < nk) issue_any(slot(J_), kt + 4);
-      read_stage(slot(std::integral_constant<int, J + 1>{}), nxt);
+      if (s + 2 < nk) issue_any(slot(J_), s + 2);
+      read_step(slot(std::integral_constant<int, J + 1>{}), 0, fr[0]);
     }
-    mfma_rows(cur, 2);
+    mfma_all(fr[1]);
   };
-  const int main_steps = nfull >= 4 ? ((nfull - 4) & ~(kStages - 1)) : 0;  // multiple of 4
-  int kt = 0;
-  for (; kt < main_steps; kt += kStages) {
-    step_main(S0{}, kt);
-    step_main(S1{}, kt + 1);
-    step_main(S2{}, kt + 2);
-    step_main(S3{}, kt + 3);
+  const int main_stages = nfull > 2 ? (nfull - 2) & ~1 : 0;  // even: buffer index is compile-time
+  int s = 0;
+  for (; s < main_stages; s += 2) {
+    stage_main(S0{}, s);
+    stage_main(S1{}, s + 1);
   }
-  for (; kt < nk; kt += kStages) {
-    step_any(S0{}, kt);
-    if (kt + 1 < nk) step_any(S1{}, kt + 1);
-    if (kt + 2 < nk) step_any(S2{}, kt + 2);
-    if (kt + 3 < nk) step_any(S3{}, kt + 3);
+  for (; s < nk; s += 2) {
+    stage_any(S0{}, s);
+    if (s + 1 < nk) stage_any(S1{}, s + 1);
   }
   wait_vmcnt<0>();
   block_sync_lds();
 
   // ---- epilogue: 2^-(ba+bb) (exact power-of-two scaling), bf16 RNE, then
-  // the 256 x 256 bf16 tile (128 KB: 64 rows of 512 bytes per slot) is
+  // the 256 x 256 bf16 tile (128 KB: 64 rows of 512 bytes per half buffer) is
   // staged row-major in LDS so the block writes C in whole 512-byte rows of
   // 16-byte stores. 16-byte chunks of each LDS row are XOR-swizzled by
   // (row & 31).
@@ -321,8 +339,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi) {
     const int row = 128 * wm + 32 * mi + frow;
-    lds_u8* crow = (mi < 2 ? (wm ? slot(S2{}) : slot(S0{})) : (wm ? slot(S3{}) : slot(S1{}))) +
-                   (row & 63) * 512;
+    lds_u8* crow = (wm ? slot(S1{}) : slot(S0{})) + (mi >> 1) * (kStageBytes / 2) + (row & 63) * 512;
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni) {
 #pragma unroll
@@ -349,9 +366,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
     }
   };
   drain(slot(S0{}), 0);
-  drain(slot(S1{}), 1);
-  drain(slot(S2{}), 2);
-  drain(slot(S3{}), 3);
+  drain(slot(S0{}) + kStageBytes / 2, 1);
+  drain(slot(S1{}), 2);
+  drain(slot(S1{}) + kStageBytes / 2, 3);
 }
 
 template <int FA, int FB>
