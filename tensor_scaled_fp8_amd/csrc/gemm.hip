@@ -154,8 +154,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
   for (int i = 0; i < 8; ++i) {
     const int row = 8 * (8 * w + i) + (lane >> 3);
     const int kc = 16 * ((lane & 7) ^ swz(row));
-    offa[i] = (uint32_t)min(m0 + row, M - 1) * (uint32_t)R + kc;
-    offb[i] = (uint32_t)min(n0 + row, N - 1) * (uint32_t)R + kc;
+    // 32-bit products, passed through an empty asm: fused into a 64-bit
+    // multiply-add, each offset would occupy a register pair
+    uint32_t pa = (uint32_t)min(m0 + row, M - 1) * (uint32_t)R;
+    uint32_t pb = (uint32_t)min(n0 + row, N - 1) * (uint32_t)R;
+    asm volatile("" : "+v"(pa), "+v"(pb));
+    offa[i] = pa + kc;
+    offb[i] = pb + kc;
   }
   const int nk = (R + kBK - 1) / kBK;      // stages
   const int nfull = R / kBK;               // full stages (all but a partial last one)
@@ -242,13 +247,26 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.0f;
 
+  // Dequantisation 2^s, s = -(ba + bb). Where it cannot take any product or
+  // FP32 partial sum out of the normal range, it is applied by the MFMA's
+  // own operand scales (E8M0 exponents 127 - ba and 127 - bb): every
+  // product and partial sum is a multiple of the smallest FP8 product
+  // (>= 2^-32) and at most R * 2^25 in size, so for -94 <= s <= 72 each value
+  // scales exactly and every FP32 rounding commutes with the scaling; the
+  // result equals accumulate-then-scale bit for bit and the epilogue skips
+  // its 256 ldexp per lane. Otherwise the operand scales are 1.0 (127) and
+  // the epilogue scales.
+  const int ba = sa->bias, bb = sb->bias;
+  const int shift = -(ba + bb);
+  const bool fold = shift >= -94 && shift <= 72;
+  const int esa = fold ? 127 - ba : 127, esb = fold ? 127 - bb : 127;
   auto mfma_all = [&](const Frags& f) {
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
       for (int ni = 0; ni < 4; ++ni)
         acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[ni], f.a[mi], acc[mi][ni], FB, FA,
-                                                                       0, 0, 0, 0);
+                                                                       0, esb, 0, esa);
   };
 
   // Software pipeline. Stage s lives in buffer s % 2; its two MFMA steps use
@@ -302,18 +320,20 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
     for (int i = 0; i < 8; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     __builtin_amdgcn_sched_barrier(0);
   };
-  // general stage (tail): bounds on every stage; zero-filled parts of a
-  // partial stage are LDS stores, made visible by the next barrier
-  // (block_sync_lds waits for this wave's LDS accesses first)
-  auto stage_any = [&](auto J_, int s) {
-    constexpr int J = decltype(J_)::value;
-    read_step(slot(J_), 1, fr[1]);
+  // general stage (tail, at most a few stages): bounds on every stage, all
+  // loads awaited in full, so the buffers are picked at run time; zero-filled
+  // parts of a partial stage are LDS stores, made visible by the next
+  // barrier (block_sync_lds waits for this wave's LDS accesses first)
+  auto stage_any = [&](int s) {
+    lds_u8* cur = (s & 1) ? slot(S1{}) : slot(S0{});
+    lds_u8* nxt = (s & 1) ? slot(S0{}) : slot(S1{});
+    read_step(cur, 1, fr[1]);
     mfma_all(fr[0]);
     if (s + 1 < nk) {
       wait_vmcnt<0>();
       block_sync_lds();
-      if (s + 2 < nk) issue_any(slot(J_), s + 2);
-      read_step(slot(std::integral_constant<int, J + 1>{}), 0, fr[0]);
+      if (s + 2 < nk) issue_any(cur, s + 2);
+      read_step(nxt, 0, fr[0]);
     }
     mfma_all(fr[1]);
   };
@@ -323,52 +343,81 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
     stage_main(S0{}, s);
     stage_main(S1{}, s + 1);
   }
-  for (; s < nk; s += 2) {
-    stage_any(S0{}, s);
-    if (s + 1 < nk) stage_any(S1{}, s + 1);
-  }
+  for (; s < nk; ++s) stage_any(s);
   wait_vmcnt<0>();
   block_sync_lds();
 
-  // ---- epilogue: 2^-(ba+bb) (exact power-of-two scaling), bf16 RNE, then
-  // the 256 x 256 bf16 tile (128 KB: 64 rows of 512 bytes per half buffer) is
-  // staged row-major in LDS so the block writes C in whole 512-byte rows of
-  // 16-byte stores. 16-byte chunks of each LDS row are XOR-swizzled by
-  // (row & 31).
-  const int shift = -(sa->bias + sb->bias);
+  // ---- epilogue: 2^s if not folded into the MFMAs (exact power-of-two
+  // scaling), bf16 RNE, then the 256 x 256 bf16 tile (128 KB: 64 rows of 512
+  // bytes per half buffer) is staged row-major in LDS so the block writes C
+  // in whole 512-byte rows of 16-byte stores. 16-byte chunks of each LDS row
+  // are XOR-swizzled by (row & 31).
+  auto stage_c = [&](auto SCALE_) {
+    constexpr bool SCALE = decltype(SCALE_)::value;
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi) {
-    const int row = 128 * wm + 32 * mi + frow;
-    lds_u8* crow = (wm ? slot(S1{}) : slot(S0{})) + (mi >> 1) * (kStageBytes / 2) + (row & 63) * 512;
+    for (int mi = 0; mi < 4; ++mi) {
+      const int row = 128 * wm + 32 * mi + frow;
+      lds_u8* crow = (wm ? slot(S1{}) : slot(S0{})) + (mi >> 1) * (kStageBytes / 2) + (row & 63) * 512;
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni) {
+      for (int ni = 0; ni < 4; ++ni) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        f32x2 lo = {ldexpf(acc[mi][ni][4 * q + 0], shift), ldexpf(acc[mi][ni][4 * q + 1], shift)};
-        f32x2 hi = {ldexpf(acc[mi][ni][4 * q + 2], shift), ldexpf(acc[mi][ni][4 * q + 3], shift)};
-        const uint32_t p0 = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2));
-        const uint32_t p1 = __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2));
-        const int chunk = 16 * wn + 4 * ni + q;
-        *(lds_u32x2*)(crow + ((chunk ^ (row & 31)) << 4) + 8 * g) = (u32x2){p0, p1};
+        for (int q = 0; q < 4; ++q) {
+          f32x2 lo = {acc[mi][ni][4 * q + 0], acc[mi][ni][4 * q + 1]};
+          f32x2 hi = {acc[mi][ni][4 * q + 2], acc[mi][ni][4 * q + 3]};
+          if constexpr (SCALE) {
+            lo = (f32x2){ldexpf(lo.x, shift), ldexpf(lo.y, shift)};
+            hi = (f32x2){ldexpf(hi.x, shift), ldexpf(hi.y, shift)};
+          }
+          const uint32_t p0 = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2));
+          const uint32_t p1 = __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2));
+          const int chunk = 16 * wn + 4 * ni + q;
+          *(lds_u32x2*)(crow + ((chunk ^ (row & 31)) << 4) + 8 * g) = (u32x2){p0, p1};
+        }
+        // scaling path: one 32 x 32 block at a time, which bounds how many
+        // accumulators are moved out of the accumulation registers at once
+        if constexpr (SCALE) __builtin_amdgcn_sched_barrier(0);
       }
     }
-  }
+  };
+  if (fold) stage_c(std::false_type{});
+  else stage_c(std::true_type{});
   block_sync_lds();
-  auto drain = [&](const lds_u8* src, int j) {
-#pragma unroll 4
+
+  // Drain: lane t takes 16-byte chunk c = t % 32 of rows r0 + 8k (r0 = t / 32)
+  // of each 64-row region. The LDS swizzle of row 64j + r0 + 8k is
+  // r0 + 8 (k % 4), so four per-lane LDS offsets plus immediates address
+  // every read; the global pointer steps 8 rows per store.
+  // (the thread index is passed through an empty asm so that none of this
+  // address arithmetic is hoisted above the k-loop, where registers are full)
+  int te = t;
+  asm volatile("" : "+v"(te));
+  const int c = te & 31, r0 = te >> 5;
+  int loff[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) loff[kk] = (r0 + 8 * kk) * 512 + ((c ^ (r0 + 8 * kk)) << 4);
+  const bool full_tile = m0 + kBM <= M && n0 + kBN <= N;
+  const bool col_ok = n0 + 8 * c < N;
+  uint16_t* cp = C + (int64_t)(m0 + r0) * N + n0 + 8 * c;
+  const int64_t step8 = (int64_t)8 * N;
+  auto drain = [&](const lds_u8* src, int j, auto FULL_) {
+    constexpr bool FULL = decltype(FULL_)::value;
+    u32x4 v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = *(const lds_u32x4*)(src + loff[k & 3] + (k >> 2) * 16384);
+#pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const int q = t + kThreads * k;        // 2048 chunks of 16 bytes per slot
-      const int lrow = q >> 5, c = q & 31;   // 64 rows x 32 chunks
-      const int row = 64 * j + lrow;
-      const u32x4 v = *(const lds_u32x4*)(src + lrow * 512 + ((c ^ (row & 31)) << 4));
-      const int grow = m0 + row, gcol = n0 + 8 * c;
-      if (grow < M && gcol < N) *(u32x4*)(C + (int64_t)grow * N + gcol) = v;
+      if (FULL || (col_ok && m0 + 64 * j + r0 + 8 * k < M)) *(u32x4*)cp = v[k];
+      cp += step8;
     }
   };
-  drain(slot(S0{}), 0);
-  drain(slot(S0{}) + kStageBytes / 2, 1);
-  drain(slot(S1{}), 2);
-  drain(slot(S1{}) + kStageBytes / 2, 3);
+  auto drain_all = [&](auto FULL_) {
+    drain(slot(S0{}), 0, FULL_);
+    drain(slot(S0{}) + kStageBytes / 2, 1, FULL_);
+    drain(slot(S1{}), 2, FULL_);
+    drain(slot(S1{}) + kStageBytes / 2, 3, FULL_);
+  };
+  if (full_tile) drain_all(std::true_type{});
+  else drain_all(std::false_type{});
 }
 
 template <int FA, int FB>

@@ -237,6 +237,24 @@ def test_gemm_extremes_saturated_operands():
     _gemm_check(A, 0, 20, B, 1, 30)
 
 
+@pytest.mark.parametrize("shift", [-252, -140, -95, -94, -60, 0, 40, 72, 73, 100])
+@pytest.mark.parametrize("fa,fb", [(0, 0), (1, 0), (0, 1), (1, 1)])
+def test_gemm_dequant_scale_range(shift, fa, fb):
+    """2^-(ba+bb) across the whole bias range, on both sides of the range the
+    kernel folds into the MFMA operand scales ([-94, 72]): outputs that
+    underflow to zero, land on bf16 subnormals, or sit near the top of the
+    bf16 range all follow the oracle's single rounding."""
+    g = np.random.Generator(np.random.PCG64(1000 + shift + 4 * fa + fb))
+    ba = -shift // 2
+    bb = -shift - ba
+    A = g.choice(_finite_codes(FMT[fa]), size=(80, 320))
+    B = g.choice(_finite_codes(FMT[fb]), size=(48, 320))
+    if shift >= 72:   # keep |C| below the bf16 maximum
+        A = np.where(np.abs(oracle.decode_table(FMT[fa])[A]) > 4, 0, A).astype(np.uint8)
+        B = np.where(np.abs(oracle.decode_table(FMT[fb])[B]) > 4, 0, B).astype(np.uint8)
+    _gemm_check(A, fa, ba, B, fb, bb)
+
+
 def test_gemm_degenerate():
     s = scale_record(0)
     a = torch.zeros((32, 0), dtype=torch.uint8, device="cuda")
