@@ -102,25 +102,26 @@ def main():
         """instrument: None, "gemm" (events around the GEMM launches) or "all"."""
         for d in lin:
             L, ws = d["L"], d["ws"]
+            n = L.name
             seq = [
-                ("quant", 6 * L.M * L.K, 0,
+                ("quant", f"{n}.X", 6 * L.M * L.K, 0,
                  lambda: tsf.fp8_quantize(d["X"], "e4m3", ws.sx, margin, 0, ws.x8, ws.x8t)),
-                ("quant", 6 * L.K * L.N, 0,
+                ("quant", f"{n}.W", 6 * L.K * L.N, 0,
                  lambda: tsf.fp8_quantize(d["W"], "e4m3", ws.sw, margin, 0, ws.w8, ws.w8t)),
-                ("gemm", 0, 2 * L.M * L.N * L.K,
+                ("gemm", f"{n}.fwd {L.M}x{L.N}x{L.K}", 0, 2 * L.M * L.N * L.K,
                  lambda: tsf.fp8_gemm_nt(ws.x8, "e4m3", ws.sx, ws.w8t, "e4m3", ws.sw, d["Y"])),
-                ("quant", 6 * L.M * L.N, 0,
+                ("quant", f"{n}.dY", 6 * L.M * L.N, 0,
                  lambda: tsf.fp8_quantize(d["dY"], "e5m2", ws.sdy, margin, mu, ws.dy8, ws.dy8t)),
-                ("gemm", 0, 2 * L.M * L.K * L.N,
+                ("gemm", f"{n}.dgrad {L.M}x{L.K}x{L.N}", 0, 2 * L.M * L.K * L.N,
                  lambda: tsf.fp8_gemm_nt(ws.dy8, "e5m2", ws.sdy, ws.w8, "e4m3", ws.sw, d["dX"])),
-                ("gemm", 0, 2 * L.K * L.N * L.M,
+                ("gemm", f"{n}.wgrad {L.K}x{L.N}x{L.M}", 0, 2 * L.K * L.N * L.M,
                  lambda: tsf.fp8_gemm_nt(ws.x8t, "e4m3", ws.sx, ws.dy8t, "e5m2", ws.sdy, d["dW"])),
             ]
-            for kind, nbytes, flops, fn in seq:
+            for kind, label, nbytes, flops, fn in seq:
                 if instrument == "all" or (instrument == "gemm" and kind == "gemm"):
                     e0 = hip.record()
                     fn()
-                    events.append((kind, nbytes, flops, e0, hip.record()))
+                    events.append((kind, label, nbytes, flops, e0, hip.record()))
                 else:
                     fn()
 
@@ -144,7 +145,7 @@ def main():
     ms = (t1 - t0) * 1e3 / args.steps
     flops = wl.flops_fwd_bwd()
     value = flops / (ms * 1e-3) / 1e12
-    timed = [(k, b, f, hip.elapsed_ms(e0, e1)) for k, b, f, e0, e1 in events]
+    timed = [(k, lb, b, f, hip.elapsed_ms(e0, e1)) for k, lb, b, f, e0, e1 in events]
     # breakdown pass: the same steps with events around every launch (amax
     # and cast figures; these events cost a little time, so this pass is
     # kept out of the timed region)
@@ -152,11 +153,12 @@ def main():
     for _ in range(args.breakdown_steps):
         step("all")
     torch.cuda.synchronize()
-    brk = [(k, b, f, hip.elapsed_ms(e0, e1)) for k, b, f, e0, e1 in events]
+    brk = [(k, lb, b, f, hip.elapsed_ms(e0, e1)) for k, lb, b, f, e0, e1 in events]
+    infer = inference_pass(tsf, torch, lin, margin, args.steps, args.warmup)
 
     def aggregate(rows):
         agg = {}
-        for kind, nbytes, fl, t in rows:
+        for kind, _, nbytes, fl, t in rows:
             a = agg.setdefault(kind, {"ms": 0.0, "bytes": 0, "flops": 0, "n": 0})
             a["ms"] += t
             a["bytes"] += nbytes
@@ -180,6 +182,14 @@ def main():
                             "avg_call_us": round(a["ms"] * 1e3 / a["n"], 2),
                             "bytes": "6 per element: amax read 2, cast read 2, two FP8 copies 2"}
     kernels["gemm"] = {"TFLOP/s": round(gemm_tflops, 1), "ms_per_step": round(g["ms"] / args.steps, 4)}
+    per = {}
+    for kind, label, _, fl, t in timed:
+        if kind == "gemm":
+            p = per.setdefault(label, [0.0, 0, fl])
+            p[0] += t
+            p[1] += 1
+    kernels["gemm_by_launch"] = {lb: {"us": round(t * 1e3 / n, 1), "TFLOP/s": round(fl / (t / n * 1e-3) / 1e12, 1)}
+                                 for lb, (t, n, fl) in per.items()}
     kernels["note"] = ("gemm: events in the timed region; amax+cast (fp8_quantize: amax pass + "
                        f"cast kernel): a separate pass of {args.breakdown_steps} steps with events "
                        "around every call")
@@ -205,11 +215,43 @@ def main():
         "cpu_baseline": cpu,
         "kernels": kernels,
         "frac_fp8_peak_step": round(value / PEAK_FP8_TFLOPS, 4),
+        "inference": infer,
         "input_gen_s": round(t_gen, 1),
     }
     if check is not None:
         out["check"] = check
     print(json.dumps(out), flush=True)
+
+
+def inference_pass(tsf, torch, lin, margin, steps, warmup):
+    """Forward-only inference on weights cast once (post-training
+    quantisation): per linear, fp8_linear_fwd_cached = X quantised (amax
+    rule, or a fixed FP8-CSCALE bias) + the forward GEMM on the cached w8t.
+    Reported beside the training step, not part of its value."""
+    out = {}
+    flops = sum(2 * d["L"].M * d["L"].K * d["L"].N for d in lin)
+    recs = tsf.new_scale(len(lin), lin[0]["X"].device)
+    for mode in ("amax", "fixed"):
+        if mode == "fixed":
+            for i, d in enumerate(lin):   # the bias the amax rule chose, now held fixed
+                recs[i].copy_(d["ws"].sx)
+
+        def fwd():
+            for i, d in enumerate(lin):
+                ws = d["ws"]
+                tsf.fp8_linear_fwd_cached(d["X"], ws.w8t, ws.sw, ws.x8, recs[i], margin, mode, Y=d["Y"])
+        for _ in range(warmup):
+            fwd()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            fwd()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+        out[mode] = {"ms_per_forward": round(ms, 4), "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 1)}
+    out["note"] = ("forward only, weights cast once (w8t, sw from the training step): X scaled from its "
+                   "amax per call, or with a fixed bias (FP8-CSCALE); 2*M*K*N per linear")
+    return out
 
 
 class HipEvents:

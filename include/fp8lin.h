@@ -17,6 +17,10 @@
  *           configurable margin (bullet 2); scale before the FP8 cast and
  *           undo the scaling after the matmul (bullet 3); E4 format for
  *           weights and activations, E5 for gradients (bullet 4).
+ *           The method also serves inference by post-training
+ *           quantisation (bullet 5), and is compared with a fixed scaling
+ *           bias, FP8-CSCALE (bullet 6; section "Main results", bullet 3:
+ *           at 13B parameters a fixed bias converges only in [-1, 0]).
  *   [FP8LM] reading note on Peng et al., "FP8-LM: Training FP8 Large
  *           Language Models", section "Proposed method", O1, Eq. 3:
  *           gradients are multiplied by an auto-scaling factor mu.
@@ -46,7 +50,7 @@
 extern "C" {
 #endif
 
-#define FP8LIN_ABI_VERSION 2
+#define FP8LIN_ABI_VERSION 3
 
 typedef enum fp8_fmt {
   FP8_E4M3 = 0, /* OCP E4M3FN: weights and activations [AMAX bullet 4] */
@@ -152,6 +156,17 @@ fp8_status fp8_quantize(const void* x_bf16, int64_t rows, int64_t cols, fp8_fmt 
                         hipStream_t stream);
 
 /*
+ * FP8-CSCALE fixed scaling [AMAX "Proposed method" bullet 6, "Main results"
+ * bullet 3]: set a record to a constant bias instead of deriving it from the
+ * tensor's amax. Writes amax = 0, bias, scale = 2^bias, scale_inv = 2^-bias,
+ * flags = 0 (the internal words are left as they are), so that fp8_cast and
+ * fp8_gemm_nt use the record exactly as they use an amax-derived one.
+ *   s_dev  device record, 16-B aligned.
+ *   bias   in [-126, 126], else FP8_ERR_INVALID.
+ */
+fp8_status fp8_scale_fixed(fp8_scale_t* s_dev, int32_t bias, hipStream_t stream);
+
+/*
  * a3 - cast (+ transpose) [AMAX bullets 3-4]: q = enc_fmt(x * 2^bias) with
  * round-to-nearest-even, saturation to +-max, subnormals kept, NaN ->
  * 0x7F|sign; bias from s_dev (device).
@@ -220,6 +235,30 @@ fp8_status fp8_linear_fwd(const void* X, const void* W, int64_t M, int64_t K, in
  */
 fp8_status fp8_linear_bwd(const void* dY, int64_t M, int64_t K, int64_t N, int margin, int mu_log2,
                           const fp8_linear_ws* ws, void* dX, void* dW, hipStream_t stream);
+
+/* How fp8_linear_fwd_cached scales X. */
+typedef enum fp8_scaling {
+  FP8_SCALING_AMAX = 0,  /* just in time from amax(X) and the margin (FP8-AMAX) */
+  FP8_SCALING_FIXED = 1  /* the bias already in sx, e.g. from fp8_scale_fixed (FP8-CSCALE) */
+} fp8_scaling;
+
+/*
+ * FP8 inference forward with a weight cast once, as in post-training
+ * quantisation [AMAX "Proposed method" bullet 5]: Y = X W from a prepared
+ * w8t [N,K] (E4M3, e.g. fp8_amax_scale + fp8_cast of W's transposed copy,
+ * or fp8_scale_fixed + fp8_cast) and its record sw. Per call only X is
+ * quantised: with FP8_SCALING_AMAX, amax + bias (margin) + the row-wise cast
+ * into x8 with its record written to sx (as fp8_quantize with no transposed
+ * output); with FP8_SCALING_FIXED, the row-wise cast with the bias sx holds.
+ * Then the forward GEMM. Bit-identical to fp8_linear_fwd's Y when w8t and
+ * sw are what fp8_linear_fwd would produce from W.
+ *   X [M,K] bf16, Y [M,N] bf16, w8t [N,K] u8, x8 [M,K] u8; device, 16-B
+ *   aligned. M, K, N multiples of 16, x8 and w8t below 4 GiB.
+ *   sw: read only. sx: written (AMAX) or read (FIXED).
+ */
+fp8_status fp8_linear_fwd_cached(const void* X, int64_t M, int64_t K, int64_t N, int margin,
+                                 fp8_scaling x_scaling, const uint8_t* w8t, const fp8_scale_t* sw,
+                                 uint8_t* x8, fp8_scale_t* sx, void* Y, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -83,6 +83,14 @@ def scale_record(bits, fmt: Fp8Format, margin: int = 0, mu_log2: int = 0) -> dic
     return {"amax": a, "bias": b, "scale": 2.0 ** b, "scale_inv": 2.0 ** -b, "flags": flags}
 
 
+def fixed_record(bias: int) -> dict:
+    """FP8-CSCALE [AMAX "Proposed method" bullet 6]: the record of a constant
+    scaling bias, set without looking at the tensor (amax 0, no flags)."""
+    if not BIAS_MIN <= bias <= BIAS_MAX:
+        raise ValueError("bias outside [-126, 126]")
+    return {"amax": 0.0, "bias": bias, "scale": 2.0 ** bias, "scale_inv": 2.0 ** -bias, "flags": 0}
+
+
 def cast(bits, fmt: Fp8Format, bias: int):
     """FP8 codes of t * 2^bias for a bf16 matrix [R, C]: (row-wise [R, C],
     transposed [C, R]). The product is exact in float64."""

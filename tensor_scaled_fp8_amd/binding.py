@@ -3,8 +3,9 @@ marshalling only. Torch supplies device memory and the current HIP stream;
 every step of the computation runs in the HIP kernels of libfp8lin.so.
 
 Names follow the C entry points: fp8_amax, fp8_scale, fp8_amax_scale,
-fp8_cast, fp8_gemm_nt, fp8_quantize, fp8_linear_fwd, fp8_linear_bwd. A scaling record
-(fp8_scale_t, 64 bytes) is an int32 tensor of 16 words on the device."""
+fp8_scale_fixed, fp8_cast, fp8_gemm_nt, fp8_quantize, fp8_linear_fwd,
+fp8_linear_bwd, fp8_linear_fwd_cached. A scaling record (fp8_scale_t, 64
+bytes) is an int32 tensor of 16 words on the device."""
 from __future__ import annotations
 
 import ctypes
@@ -13,9 +14,10 @@ from typing import Optional
 import torch
 
 from . import _lib
-from ._lib import FP8_E4M3, FP8_E5M2, LinearWs, check, load
+from ._lib import FP8_E4M3, FP8_E5M2, FP8_SCALING_AMAX, FP8_SCALING_FIXED, LinearWs, check, load
 
 SCALE_WORDS = 16         # sizeof(fp8_scale_t) / 4
+SCALINGS = {"amax": FP8_SCALING_AMAX, "fixed": FP8_SCALING_FIXED}
 FMT_CODES = {"e4m3": FP8_E4M3, "e5m2": FP8_E5M2, FP8_E4M3: FP8_E4M3, FP8_E5M2: FP8_E5M2}
 
 
@@ -80,6 +82,11 @@ def fp8_bias_host(amax: float, fmt, margin: int = 0, mu_log2: int = 0):
     flags = ctypes.c_uint32(0)
     b = load().fp8_bias_host(float(amax), _fmt(fmt), margin, mu_log2, ctypes.byref(flags))
     return int(b), int(flags.value)
+
+
+def fp8_scale_fixed(s: torch.Tensor, bias: int) -> None:
+    """FP8-CSCALE: set the record to a constant bias (scale 2^bias)."""
+    check(load().fp8_scale_fixed(_dev(s, torch.int32, "s"), int(bias), _stream(s)), "fp8_scale_fixed")
 
 
 def fp8_cast(x: torch.Tensor, fmt, s: torch.Tensor, out_row: Optional[torch.Tensor] = None,
@@ -225,3 +232,69 @@ class Linear(torch.nn.Module):
 
     def forward(self, x):
         return linear(x, self.weight, self.margin, self.mu_log2)
+
+
+def prepare_weight(W: torch.Tensor, margin: int = 0, fixed_bias: Optional[int] = None):
+    """Cast a bf16 weight W [K, N] once for inference (post-training
+    quantisation): returns (w8t [N, K] E4M3 codes, record sw). The bias comes
+    from amax(W) and the margin, or is fixed_bias (FP8-CSCALE)."""
+    if W.dim() != 2:
+        raise ValueError("W must be 2-D")
+    sw = new_scale(1, W.device)[0]
+    if fixed_bias is None:
+        fp8_amax_scale(W, "e4m3", sw, margin)
+    else:
+        fp8_scale_fixed(sw, fixed_bias)
+    _, w8t = fp8_cast(W, "e4m3", sw, rowwise=False, transposed=True)
+    return w8t, sw
+
+
+def fp8_linear_fwd_cached(X: torch.Tensor, w8t: torch.Tensor, sw: torch.Tensor, x8: torch.Tensor,
+                          sx: torch.Tensor, margin: int = 0, x_scaling: str = "amax",
+                          Y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Y [M, N] = X [M, K] W from a prepared w8t [N, K] and its record sw.
+    x_scaling "amax": X's bias from amax(X) and the margin (written to sx);
+    "fixed": the bias already in sx (fp8_scale_fixed)."""
+    if X.dim() != 2 or w8t.dim() != 2 or X.shape[1] != w8t.shape[1]:
+        raise ValueError(f"shape mismatch: X {tuple(X.shape)}, w8t {tuple(w8t.shape)}")
+    M, K = X.shape
+    N = w8t.shape[0]
+    if tuple(x8.shape) != (M, K):
+        raise ValueError("x8 must be [M, K]")
+    try:
+        mode = SCALINGS[x_scaling]
+    except KeyError:
+        raise ValueError(f"unknown x_scaling {x_scaling!r}") from None
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device=X.device)
+    check(load().fp8_linear_fwd_cached(_dev(X, torch.bfloat16, "X"), M, K, N, margin, mode,
+                                       _dev(w8t, torch.uint8, "w8t"), _dev(sw, torch.int32, "sw"),
+                                       _dev(x8, torch.uint8, "x8"), _dev(sx, torch.int32, "sx"),
+                                       _dev(Y, torch.bfloat16, "Y"), _stream(X)), "fp8_linear_fwd_cached")
+    return Y
+
+
+class InferenceLinear(torch.nn.Module):
+    """Forward-only FP8 linear on a weight cast once (post-training
+    quantisation). X is scaled from its amax per call, or with a fixed bias
+    (FP8-CSCALE) when x_fixed_bias is given."""
+
+    def __init__(self, W: torch.Tensor, margin: int = 0, w_fixed_bias: Optional[int] = None,
+                 x_fixed_bias: Optional[int] = None):
+        super().__init__()
+        self.margin = margin
+        self.w8t, self.sw = prepare_weight(W, margin, w_fixed_bias)
+        self.sx = new_scale(1, W.device)[0]
+        self.x_scaling = "amax"
+        if x_fixed_bias is not None:
+            fp8_scale_fixed(self.sx, x_fixed_bias)
+            self.x_scaling = "fixed"
+        self._x8 = None
+
+    def forward(self, x: torch.Tensor) -> torch.Tensor:
+        shape = x.shape
+        x2 = x.reshape(-1, shape[-1]).contiguous()
+        if self._x8 is None or tuple(self._x8.shape) != tuple(x2.shape):
+            self._x8 = torch.empty(x2.shape, dtype=torch.uint8, device=x2.device)
+        y = fp8_linear_fwd_cached(x2, self.w8t, self.sw, self._x8, self.sx, self.margin, self.x_scaling)
+        return y.reshape(*shape[:-1], y.shape[-1])

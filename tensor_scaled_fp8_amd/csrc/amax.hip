@@ -147,6 +147,16 @@ __global__ void scale_kernel(fp8_scale_t* s, int fmt, int margin, int mu_log2) {
   s->flags = flags;
 }
 
+// FP8-CSCALE: a constant bias instead of the amax rule; the internal words
+// are left alone so the record stays usable by the amax paths
+__global__ void scale_fixed_kernel(fp8_scale_t* s, int32_t b) {
+  s->amax = 0.0f;
+  s->bias = b;
+  s->scale = pow2f(b);
+  s->scale_inv = pow2f(-b);
+  s->flags = 0u;
+}
+
 __global__ void scale_reset_kernel(uint4* s, int64_t n16) {
   int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n16) s[i] = make_uint4(0, 0, 0, 0);
@@ -195,6 +205,11 @@ hipError_t launch_amax_gen(const void* x, int64_t n, fp8_scale_t* s, uint64_t ge
   const SweepGrid g = sweep_grid(x, n);
   hipLaunchKernelGGL(amax_gen_kernel, dim3((unsigned)g.blocks), dim3(kThreads), 0, st, (const u32x4*)x,
                      g.n_vec, g.per_block, g.tail, g.tail_n, s, gen);
+  return hipGetLastError();
+}
+
+hipError_t launch_scale_fixed(fp8_scale_t* s, int32_t bias, hipStream_t st) {
+  hipLaunchKernelGGL(scale_fixed_kernel, dim3(1), dim3(1), 0, st, s, bias);
   return hipGetLastError();
 }
 

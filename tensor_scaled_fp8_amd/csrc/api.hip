@@ -79,6 +79,11 @@ int32_t fp8_bias_host(float amax, fp8_fmt fmt, int margin, int mu_log2, uint32_t
   return bias_from_amax_bits(bits & 0x7FFFFFFFu, fmt, margin, mu_log2, flags_out);
 }
 
+fp8_status fp8_scale_fixed(fp8_scale_t* s_dev, int32_t bias, hipStream_t stream) {
+  if (!s_dev || !aligned16(s_dev) || bias < -126 || bias > 126) return FP8_ERR_INVALID;
+  return hip_status(launch_scale_fixed(s_dev, bias, stream));
+}
+
 fp8_status fp8_cast(const void* x_bf16, int64_t rows, int64_t cols, fp8_fmt fmt,
                     const fp8_scale_t* s_dev, uint8_t* out_rowwise, uint8_t* out_transposed,
                     hipStream_t stream) {
@@ -176,6 +181,24 @@ fp8_status fp8_linear_bwd(const void* dY, int64_t M, int64_t K, int64_t N, int m
                 hipSuccess)
     return FP8_ERR_HIP;
   return FP8_OK;
+}
+
+fp8_status fp8_linear_fwd_cached(const void* X, int64_t M, int64_t K, int64_t N, int margin,
+                                 fp8_scaling x_scaling, const uint8_t* w8t, const fp8_scale_t* sw,
+                                 uint8_t* x8, fp8_scale_t* sx, void* Y, hipStream_t stream) {
+  if (M < 0 || K < 0 || N < 0 || !int_ok(margin)) return FP8_ERR_INVALID;
+  if (x_scaling != FP8_SCALING_AMAX && x_scaling != FP8_SCALING_FIXED) return FP8_ERR_INVALID;
+  if (!sw || !aligned16(sw) || !sx || !aligned16(sx)) return FP8_ERR_INVALID;
+  if (M % 16 || K % 16 || N % 16 || M >= kMaxDim || K >= kMaxDim || N >= kMaxDim || !gemm_fits(M, N, K))
+    return FP8_ERR_UNSUPPORTED;
+  if ((M * K > 0 && (!X || !aligned16(X) || !x8 || !aligned16(x8))) ||
+      (N * K > 0 && (!w8t || !aligned16(w8t))) || (M * N > 0 && (!Y || !aligned16(Y))))
+    return FP8_ERR_INVALID;
+  hipError_t e = x_scaling == FP8_SCALING_AMAX
+                     ? launch_quantize(X, M, K, FP8_E4M3, margin, 0, sx, x8, nullptr, next_generation(), stream)
+                     : launch_cast(X, M, K, FP8_E4M3, sx, x8, nullptr, stream);
+  if (e != hipSuccess) return FP8_ERR_HIP;
+  return hip_status(launch_gemm(x8, FP8_E4M3, sx, w8t, FP8_E4M3, sw, M, N, K, Y, stream));
 }
 
 }  // extern "C"

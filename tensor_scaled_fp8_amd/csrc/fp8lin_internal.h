@@ -65,6 +65,7 @@ hipError_t launch_scale_reset(fp8_scale_t* s, int64_t count, hipStream_t st);
 hipError_t launch_amax(const void* x, int64_t n, fp8_scale_t* s, bool fuse_scale, int fmt, int margin,
                        int mu_log2, hipStream_t st);
 hipError_t launch_scale(fp8_scale_t* s, int fmt, int margin, int mu_log2, hipStream_t st);
+hipError_t launch_scale_fixed(fp8_scale_t* s, int32_t bias, hipStream_t st);
 hipError_t launch_cast(const void* x, int64_t rows, int64_t cols, int fmt, const fp8_scale_t* s,
                        uint8_t* out_row, uint8_t* out_t, hipStream_t st);
 hipError_t launch_amax_gen(const void* x, int64_t n, fp8_scale_t* s, uint64_t gen, hipStream_t st);

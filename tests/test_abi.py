@@ -31,7 +31,7 @@ def test_header_functions_all_exported():
     for n in names:
         assert hasattr(lib, n), n
         assert n in _lib.SIGNATURES, f"binding lacks {n}"
-    assert lib.fp8_abi_version() == 2
+    assert lib.fp8_abi_version() == 3
 
 
 def test_status_strings():
@@ -102,6 +102,24 @@ def test_argument_validation_without_launch():
     assert lib.fp8_linear_fwd(_vp(ok), _vp(ok), 16, 24, 16, 0, ctypes.byref(ws), _vp(ok), None) == UNS
     ws_bad = _lib.LinearWs(ok, ok, ok, ok, None, ok, ok, ok, ok)
     assert lib.fp8_linear_bwd(_vp(ok), 16, 16, 16, 0, 0, ctypes.byref(ws_bad), None, None, None) == INV
+    # fixed bias: only [-126, 126]
+    assert lib.fp8_scale_fixed(_vp(ok), 127, None) == INV
+    assert lib.fp8_scale_fixed(_vp(ok), -127, None) == INV
+    assert lib.fp8_scale_fixed(None, 0, None) == INV
+    assert lib.fp8_scale_fixed(_vp(ok + 4), 0, None) == INV
+    # cached-weight forward
+    c = lib.fp8_linear_fwd_cached
+    args = lambda **kw: [kw.get(k, d) for k, d in (
+        ("X", _vp(ok)), ("M", 16), ("K", 16), ("N", 16), ("margin", 0), ("mode", 0), ("w8t", _vp(ok)),
+        ("sw", _vp(ok)), ("x8", _vp(ok)), ("sx", _vp(ok)), ("Y", _vp(ok)), ("st", None))]
+    assert c(*args(mode=2)) == INV
+    assert c(*args(K=24)) == UNS
+    assert c(*args(sw=None)) == INV
+    assert c(*args(sx=_vp(ok + 8))) == INV
+    assert c(*args(x8=None)) == INV
+    assert c(*args(w8t=None)) == INV
+    assert c(*args(Y=_vp(ok + 2))) == INV
+    assert c(*args(margin=-5000)) == INV
 
 
 def test_binding_rejects_cpu_tensors():

@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 
 from oracle import (E4M3, E5M2, FLAG_CLAMPED, FLAG_NONFINITE, FLAG_ZERO, amax, bf16_to_f64,
-                    cast, compute_bias, encode, scale_record)
+                    cast, compute_bias, encode, f64_to_bf16_rne, fixed_record, scale_record)
 from tests import _golden
 from workloads import f32_to_bf16_bits, random_bf16_bits
 
@@ -125,3 +125,25 @@ def test_cast_scaling_direction_keeps_amax_in_range():
             from oracle import decode_table
             dq = np.abs(decode_table(fmt)[q])
             assert fmt.max_finite / 2 <= dq.max() <= fmt.max_finite
+
+
+def test_fixed_record_matches_amax_record_of_a_tensor_at_that_bias():
+    """FP8-CSCALE: a fixed bias b gives the same scale and inverse as the
+    amax rule on a tensor whose amax is fmt_max * 2^-b (where the rule lands
+    exactly on b at margin 0), for every bias in range."""
+    for fmt in (E4M3, E5M2):
+        for b in range(-126, 127):
+            a = fmt.max_finite * 2.0 ** -b
+            if not (2.0 ** -133 <= a < 2.0 ** 128):
+                continue
+            bits = f64_to_bf16_rne(np.array([a, -a / 3]))
+            if bf16_to_f64(bits)[0] != a:
+                continue
+            want = scale_record(bits, fmt)
+            got = fixed_record(b)
+            assert want["bias"] == b and want["flags"] == 0
+            assert (got["bias"], got["scale"], got["scale_inv"], got["flags"]) == (
+                b, want["scale"], want["scale_inv"], 0)
+    for bad in (-127, 127):
+        with pytest.raises(ValueError):
+            fixed_record(bad)
