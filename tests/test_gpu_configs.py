@@ -9,8 +9,10 @@ At these sizes the oracle checks, per linear:
     sampled rows of each transposed copy (oracle cast of those rows or
     columns), plus, on the device, transposed copy == row-wise copy
     transposed for the whole tensor (a property at any size);
-  * Y, dX, dW: 192 sampled elements each, within 1 bf16 ulp + 1e-4 *
-    sum_r |a_r b_r| of the float64 oracle on the oracle's own FP8 operands.
+  * Y, dX, dW: 192 sampled elements each, plus two whole 256 x 256 output
+    tiles (one interior tile and the last, bottom-right one, i.e. complete
+    kernel tiles), within 1 bf16 ulp + 1e-4 * sum_r |a_r b_r| of the float64
+    oracle on the oracle's own FP8 operands.
 """
 import numpy as np
 import pytest
@@ -73,6 +75,20 @@ def _check_gemm(out_dev, a_bits, fa, ba, b_bits_t, fb, bb, g):
     err = np.abs(oracle.bf16_to_f64(got) - oracle.bf16_to_f64(bits))
     bad = ~(err <= tol)
     assert not bad.any(), (int(bad.sum()), float((err / tol).max()))
+    # whole output tiles: one interior tile and the last one
+    T = 256
+    tiles = [(int(g.integers(0, max(1, M // T))) * T, int(g.integers(0, max(1, N // T))) * T),
+             (max(0, M - T), max(0, N - T))]
+    for r0, c0 in tiles:
+        rows = np.arange(r0, min(M, r0 + T))
+        cols = np.arange(c0, min(N, c0 + T))
+        qa, _ = oracle.cast(a_bits(rows), fa, ba)
+        qb, _ = oracle.cast(b_bits_t(cols), fb, bb)
+        bits, c64, tol = oracle.gemm_nt(qa, fa, ba, qb, fb, bb)
+        got = bf16_bits(out_dev[r0:r0 + len(rows), c0:c0 + len(cols)])
+        err = np.abs(oracle.bf16_to_f64(got) - oracle.bf16_to_f64(bits))
+        bad = ~(err <= tol)
+        assert not bad.any(), ("tile", r0, c0, int(bad.sum()), float((err / tol).max()))
 
 
 @pytest.mark.parametrize("wl_idx,li", CASES, ids=[f"{WORKLOADS[w].name}-{WORKLOADS[w].linears[l].name}"
