@@ -155,6 +155,7 @@ def main():
     torch.cuda.synchronize()
     brk = [(k, lb, b, f, hip.elapsed_ms(e0, e1)) for k, lb, b, f, e0, e1 in events]
     infer = inference_pass(tsf, torch, lin, margin, args.steps, args.warmup)
+    fp8dw = fp8_dw_pass(tsf, torch, lin, margin, mu, args.steps, args.warmup)
 
     def aggregate(rows):
         agg = {}
@@ -216,6 +217,7 @@ def main():
         "kernels": kernels,
         "frac_fp8_peak_step": round(value / PEAK_FP8_TFLOPS, 4),
         "inference": infer,
+        "fp8_weight_gradient": fp8dw,
         "input_gen_s": round(t_gen, 1),
     }
     if check is not None:
@@ -251,6 +253,46 @@ def inference_pass(tsf, torch, lin, margin, steps, warmup):
         out[mode] = {"ms_per_forward": round(ms, 4), "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 1)}
     out["note"] = ("forward only, weights cast once (w8t, sw from the training step): X scaled from its "
                    "amax per call, or with a fixed bias (FP8-CSCALE); 2*M*K*N per linear")
+    return out
+
+
+def fp8_dw_pass(tsf, torch, lin, margin, mu, steps, warmup):
+    """FP8 weight gradient per linear: fp8_wgrad_fp8 (wgrad GEMM whose
+    epilogue also takes max |dW|, then the E5M2 cast) against the unfused
+    wgrad GEMM + fp8_quantize(dW). Reported beside the training step."""
+    bufs = []
+    for d in lin:
+        L = d["L"]
+        bufs.append(dict(dw8=torch.empty((L.K, L.N), dtype=torch.uint8, device=d["dW"].device),
+                         s=tsf.new_scale(2, d["dW"].device)))
+    flops = sum(2 * d["L"].M * d["L"].K * d["L"].N for d in lin)
+    q_bytes = sum(3 * d["L"].K * d["L"].N for d in lin)   # E5M2 cast of dW: 2 B read + 1 B write
+
+    def fused():
+        for d, b in zip(lin, bufs):
+            ws = d["ws"]
+            tsf.fp8_wgrad_fp8(ws.x8t, ws.sx, ws.dy8t, ws.sdy, margin, mu, dW=d["dW"], s_dw=b["s"][0], dw8=b["dw8"])
+
+    def unfused():
+        for d, b in zip(lin, bufs):
+            ws = d["ws"]
+            tsf.fp8_gemm_nt(ws.x8t, "e4m3", ws.sx, ws.dy8t, "e5m2", ws.sdy, d["dW"])
+            tsf.fp8_quantize(d["dW"], "e5m2", b["s"][1], margin, mu, out_row=b["dw8"], transposed=False)
+
+    out = {}
+    for name, fn in (("fused", fused), ("unfused", unfused)):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            fn()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+        out[name] = {"ms_per_step": round(ms, 4), "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 1)}
+    out["saved_ms"] = round(out["unfused"]["ms_per_step"] - out["fused"]["ms_per_step"], 4)
+    out["note"] = ("all linears' dW in E5M2 per step: wgrad GEMM + cast (fused amax) vs wgrad GEMM + "
+                   f"fp8_quantize(dW); the cast moves {q_bytes} bytes per step")
     return out
 
 

@@ -23,7 +23,8 @@
  *           at 13B parameters a fixed bias converges only in [-1, 0]).
  *   [FP8LM] reading note on Peng et al., "FP8-LM: Training FP8 Large
  *           Language Models", section "Proposed method", O1, Eq. 3:
- *           gradients are multiplied by an auto-scaling factor mu.
+ *           gradients are multiplied by an auto-scaling factor mu, changed
+ *           dynamically (the policy is not given; see fp8_wgrad_fp8).
  *
  * Readings where the pages are silent: OCP E4M3FN (max 448, no inf) and
  * E5M2 (max 57344); encode by round-to-nearest-even with saturation to
@@ -50,7 +51,7 @@
 extern "C" {
 #endif
 
-#define FP8LIN_ABI_VERSION 3
+#define FP8LIN_ABI_VERSION 4
 
 typedef enum fp8_fmt {
   FP8_E4M3 = 0, /* OCP E4M3FN: weights and activations [AMAX bullet 4] */
@@ -95,7 +96,7 @@ typedef struct fp8_scale_t {
   uint32_t flags;
   uint32_t reduce_bits;   /* internal: running max of the |bf16| bit patterns */
   uint32_t reduce_ticket; /* internal: count of blocks that have merged */
-  uint32_t reserved;
+  uint32_t sat_count;     /* elements saturated by the last fp8_wgrad_fp8 cast */
   uint64_t gen_max;       /* internal: generation-tagged running max (fp8_quantize) */
   uint64_t reserved2[3];
 } fp8_scale_t;
@@ -235,6 +236,27 @@ fp8_status fp8_linear_fwd(const void* X, const void* W, int64_t M, int64_t K, in
  */
 fp8_status fp8_linear_bwd(const void* dY, int64_t M, int64_t K, int64_t N, int margin, int mu_log2,
                           const fp8_linear_ws* ws, void* dX, void* dW, hipStream_t stream);
+
+/*
+ * FP8 weight gradient [FP8LM "Proposed method" O1: FP8 gradients with the
+ * auto-scaling factor mu, g' = mu * g (Eq. 3); AMAX bullet 4: E5 for
+ * gradients]: dW = X^T dY (the a6 GEMM) whose epilogue also takes max |dW|
+ * over the bf16 values it writes, then dW cast to E5M2 with the bias from
+ * that amax, the margin and mu = 2^mu_log2. The result equals the wgrad
+ * GEMM followed by fp8_quantize(dW, E5M2, margin, mu_log2), without reading
+ * dW again for its amax. s_dw->sat_count is set to the number of elements
+ * whose scaled magnitude exceeded the E5M2 max (clipped to it; inf counts,
+ * NaN does not): the signal a mu auto-scaling policy needs.
+ *   x8t [K,M] E4M3 with sx, dy8t [N,M] E5M2 with sdy: as for the wgrad GEMM.
+ *   dW_bf16 [K,N] bf16: written (and read back by the cast).
+ *   dw8 [K,N] u8 E5M2: written. dw8t [N,K] u8: written, or NULL to skip.
+ *   s_dw: dW's record (written; zero its internal words once, as for any
+ *   record). K, N, M multiples of 16, operands below 4 GiB; device
+ *   pointers 16-B aligned.
+ */
+fp8_status fp8_wgrad_fp8(const uint8_t* x8t, const fp8_scale_t* sx, const uint8_t* dy8t,
+                         const fp8_scale_t* sdy, int64_t K, int64_t N, int64_t M, int margin, int mu_log2,
+                         void* dW_bf16, fp8_scale_t* s_dw, uint8_t* dw8, uint8_t* dw8t, hipStream_t stream);
 
 /* How fp8_linear_fwd_cached scales X. */
 typedef enum fp8_scaling {

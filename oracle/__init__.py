@@ -30,7 +30,7 @@ is not implemented (mu is an input).
 from .formats import E4M3, E5M2, FORMATS, Fp8Format, decode_code, decode_table, encode
 from .bf16 import bf16_to_f64, f64_to_bf16_rne, bf16_ulp
 from .scaling import (FLAG_NONFINITE, FLAG_ZERO, FLAG_CLAMPED, BIAS_MIN, BIAS_MAX,
-                      amax, compute_bias, scale_record, fixed_record, cast)
+                      amax, compute_bias, scale_record, fixed_record, saturated_count, cast)
 from .gemm import gemm_nt, gemm_nt_exact, gemm_nt_rows, tolerance
 from .linear import linear_fwd_bwd
 

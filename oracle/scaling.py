@@ -91,6 +91,14 @@ def fixed_record(bias: int) -> dict:
     return {"amax": 0.0, "bias": bias, "scale": 2.0 ** bias, "scale_inv": 2.0 ** -bias, "flags": 0}
 
 
+def saturated_count(bits, fmt: Fp8Format, bias: int) -> int:
+    """Elements that the cast clips: |t| * 2^bias above the format's max
+    (an infinity counts, a NaN does not)."""
+    x = bf16_to_f64(np.asarray(bits))
+    with np.errstate(invalid="ignore", over="ignore"):
+        return int(np.count_nonzero(np.abs(np.ldexp(x, bias)) > fmt.max_finite))
+
+
 def cast(bits, fmt: Fp8Format, bias: int):
     """FP8 codes of t * 2^bias for a bf16 matrix [R, C]: (row-wise [R, C],
     transposed [C, R]). The product is exact in float64."""

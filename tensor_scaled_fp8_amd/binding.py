@@ -4,7 +4,7 @@ every step of the computation runs in the HIP kernels of libfp8lin.so.
 
 Names follow the C entry points: fp8_amax, fp8_scale, fp8_amax_scale,
 fp8_scale_fixed, fp8_cast, fp8_gemm_nt, fp8_quantize, fp8_linear_fwd,
-fp8_linear_bwd, fp8_linear_fwd_cached. A scaling record (fp8_scale_t, 64
+fp8_linear_bwd, fp8_linear_fwd_cached, fp8_wgrad_fp8. A scaling record (fp8_scale_t, 64
 bytes) is an int32 tensor of 16 words on the device."""
 from __future__ import annotations
 
@@ -55,7 +55,8 @@ def read_scale(s: torch.Tensor) -> dict:
     f = w.view(torch.float32)
     return {"amax": float(f[0]), "bias": int(w[1]), "scale": float(f[2]),
             "scale_inv": float(f[3]), "flags": int(w[4]) & 0xFFFFFFFF,
-            "reduce_bits": int(w[5]) & 0xFFFFFFFF, "reduce_ticket": int(w[6]) & 0xFFFFFFFF}
+            "reduce_bits": int(w[5]) & 0xFFFFFFFF, "reduce_ticket": int(w[6]) & 0xFFFFFFFF,
+            "sat_count": int(w[7]) & 0xFFFFFFFF}
 
 
 def fp8_scale_reset(s: torch.Tensor) -> None:
@@ -232,6 +233,35 @@ class Linear(torch.nn.Module):
 
     def forward(self, x):
         return linear(x, self.weight, self.margin, self.mu_log2)
+
+
+def fp8_wgrad_fp8(x8t: torch.Tensor, sx: torch.Tensor, dy8t: torch.Tensor, sdy: torch.Tensor,
+                  margin: int = 0, mu_log2: int = 0, dW: Optional[torch.Tensor] = None,
+                  s_dw: Optional[torch.Tensor] = None, dw8: Optional[torch.Tensor] = None,
+                  dw8t: Optional[torch.Tensor] = None, transposed: bool = False):
+    """FP8 weight gradient: dW = X^T dY (bf16, the GEMM's epilogue also
+    takes max |dW|), then dW in E5M2 with the bias from that amax, the margin
+    and mu = 2^mu_log2. x8t [K, M], dy8t [N, M]. Returns (dW [K, N] bf16,
+    dw8 [K, N] u8, dw8t [N, K] u8 or None, s_dw)."""
+    if x8t.dim() != 2 or dy8t.dim() != 2 or x8t.shape[1] != dy8t.shape[1]:
+        raise ValueError(f"shape mismatch: x8t {tuple(x8t.shape)}, dy8t {tuple(dy8t.shape)}")
+    K, M = x8t.shape
+    N = dy8t.shape[0]
+    dev = x8t.device
+    if dW is None:
+        dW = torch.empty((K, N), dtype=torch.bfloat16, device=dev)
+    if dw8 is None:
+        dw8 = torch.empty((K, N), dtype=torch.uint8, device=dev)
+    if transposed and dw8t is None:
+        dw8t = torch.empty((N, K), dtype=torch.uint8, device=dev)
+    if s_dw is None:
+        s_dw = new_scale(1, dev)[0]
+    check(load().fp8_wgrad_fp8(_dev(x8t, torch.uint8, "x8t"), _dev(sx, torch.int32, "sx"),
+                               _dev(dy8t, torch.uint8, "dy8t"), _dev(sdy, torch.int32, "sdy"), K, N, M,
+                               margin, mu_log2, _dev(dW, torch.bfloat16, "dW"), _dev(s_dw, torch.int32, "s_dw"),
+                               _dev(dw8, torch.uint8, "dw8"), _dev(dw8t, torch.uint8, "dw8t"), _stream(x8t)),
+          "fp8_wgrad_fp8")
+    return dW, dw8, dw8t, s_dw
 
 
 def prepare_weight(W: torch.Tensor, margin: int = 0, fixed_bias: Optional[int] = None):

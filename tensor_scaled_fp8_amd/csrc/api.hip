@@ -201,4 +201,24 @@ fp8_status fp8_linear_fwd_cached(const void* X, int64_t M, int64_t K, int64_t N,
   return hip_status(launch_gemm(x8, FP8_E4M3, sx, w8t, FP8_E4M3, sw, M, N, K, Y, stream));
 }
 
+fp8_status fp8_wgrad_fp8(const uint8_t* x8t, const fp8_scale_t* sx, const uint8_t* dy8t,
+                         const fp8_scale_t* sdy, int64_t K, int64_t N, int64_t M, int margin, int mu_log2,
+                         void* dW_bf16, fp8_scale_t* s_dw, uint8_t* dw8, uint8_t* dw8t, hipStream_t stream) {
+  if (K < 0 || N < 0 || M < 0 || !int_ok(margin) || !int_ok(mu_log2)) return FP8_ERR_INVALID;
+  if (!sx || !aligned16(sx) || !sdy || !aligned16(sdy) || !s_dw || !aligned16(s_dw)) return FP8_ERR_INVALID;
+  if (K % 16 || N % 16 || M % 16 || K >= kMaxDim || N >= kMaxDim || M >= kMaxDim || !gemm_fits(K, N, M))
+    return FP8_ERR_UNSUPPORTED;
+  if (K > 0 && N > 0) {
+    if (!dW_bf16 || !aligned16(dW_bf16) || !dw8 || !aligned16(dw8)) return FP8_ERR_INVALID;
+    if (dw8t && !aligned16(dw8t)) return FP8_ERR_INVALID;
+    if (M > 0 && (!x8t || !aligned16(x8t) || !dy8t || !aligned16(dy8t))) return FP8_ERR_INVALID;
+  }
+  const uint64_t gen = next_generation();
+  hipError_t e = K > 0 && N > 0
+                     ? launch_gemm_wgrad_amax(x8t, sx, dy8t, sdy, K, N, M, dW_bf16, s_dw, gen, stream)
+                     : launch_amax_gen(nullptr, 0, s_dw, gen, stream);  // an empty max, so the record publishes
+  if (e != hipSuccess) return FP8_ERR_HIP;
+  return hip_status(launch_wgrad_cast(dW_bf16, K, N, s_dw, dw8, dw8t, margin, mu_log2, stream));
+}
+
 }  // extern "C"

@@ -80,7 +80,10 @@ __device__ inline void transpose4(const uint32_t in[4], uint32_t out[4]) {
 // DERIVE = true (fp8_quantize): every block derives it from the record's
 // generation-tagged maximum, which the amax pass just merged, with the same
 // rule as fp8_scale; block 0 publishes the record's fields.
-template <int FMT, bool DERIVE>
+// COUNT (with DERIVE): also count the elements whose scaled magnitude
+// exceeds the format's max (inf included, NaN not) into s->sat_count, which
+// the kernel before this one cleared.
+template <int FMT, bool DERIVE, bool COUNT = false>
 __global__ __launch_bounds__(kThreads) void cast_kernel(const uint16_t* __restrict__ x, int64_t rows,
                                                         int64_t cols, int64_t tiles_c, fp8_scale_t* s,
                                                         uint8_t* __restrict__ out_row,
@@ -93,6 +96,7 @@ __global__ __launch_bounds__(kThreads) void cast_kernel(const uint16_t* __restri
   const int rg = t >> 4, cc = t & 15;
   float scale;
   bool nonfinite;
+  uint32_t sat_above = 0x7F80u;  // COUNT: magnitudes above this (and <= inf) saturate
   if constexpr (DERIVE) {
     const unsigned long long word =
         __hip_atomic_load((unsigned long long*)&s->gen_max, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -100,6 +104,13 @@ __global__ __launch_bounds__(kThreads) void cast_kernel(const uint16_t* __restri
     uint32_t flags;
     const int32_t b = bias_from_amax_bits(mag << 16, FMT, margin, mu_log2, &flags);
     scale = pow2f(b);
+    if constexpr (COUNT) {
+      // fmt max = 1.75 * 2^E; max * 2^-b as a bf16 pattern: exponent field
+      // 127 + E - b, mantissa 0x60; beyond the bf16 range no finite value
+      // saturates
+      const int e = 127 + (FMT == FP8_E4M3 ? 8 : 15) - b;
+      sat_above = e <= 254 ? (((uint32_t)e << 7) | 0x60u) : 0x7F7Fu;
+    }
     nonfinite = (flags & FP8_FLAG_NONFINITE) != 0u;
     if (blockIdx.x == 0 && t == 0) {
       union { uint32_t u; float f; } a;
@@ -118,11 +129,23 @@ __global__ __launch_bounds__(kThreads) void cast_kernel(const uint16_t* __restri
   const bool ok = rr < rows && cx < cols;  // rows, cols are multiples of 16
 
   uint32_t lo[8], hi[8];
+  uint32_t nsat = 0;
   if (ok) {
     const uint16_t* src = x + rr * cols + cx;
     u32x4 v[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) v[i] = __builtin_nontemporal_load((const u32x4*)(src + i * cols));
+    if constexpr (COUNT) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t w4[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t a = w4[k] & 0x7FFFu, b2 = (w4[k] >> 16) & 0x7FFFu;
+          nsat += (a > sat_above && a <= 0x7F80u) + (b2 > sat_above && b2 <= 0x7F80u);
+        }
+      }
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       lo[i] = cvt4<FMT>(v[i].x, v[i].y, scale);
@@ -143,6 +166,22 @@ __global__ __launch_bounds__(kThreads) void cast_kernel(const uint16_t* __restri
   } else {
 #pragma unroll
     for (int i = 0; i < 8; ++i) lo[i] = hi[i] = 0u;
+  }
+  if constexpr (COUNT) {
+    // an empty tensor has no producer kernel that cleared the count
+    if ((rows == 0 || cols == 0) && t == 0) s->sat_count = 0u;
+    // block sum, one atomic per block that saw a saturation
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) nsat += (uint32_t)__shfl_xor((int)nsat, off, 64);
+    __shared__ uint32_t wsum[kThreads / 64];
+    if ((t & 63) == 0) wsum[t >> 6] = nsat;
+    __syncthreads();
+    if (t == 0) {
+      uint32_t tot = 0;
+#pragma unroll
+      for (int i = 0; i < kThreads / 64; ++i) tot += wsum[i];
+      if (tot) atomicAdd(&s->sat_count, tot);
+    }
   }
   if (!out_t) return;
 
@@ -171,18 +210,18 @@ __global__ __launch_bounds__(kThreads) void cast_kernel(const uint16_t* __restri
   }
 }
 
-template <bool DERIVE>
+template <bool DERIVE, bool COUNT = false>
 hipError_t launch_cast_t(const void* x, int64_t rows, int64_t cols, int fmt, fp8_scale_t* s,
                          uint8_t* out_row, uint8_t* out_t, int margin, int mu_log2, hipStream_t st) {
   int64_t tiles_r = (rows + kTile - 1) / kTile, tiles_c = (cols + kTile - 1) / kTile;
   if (tiles_r * tiles_c == 0) tiles_r = tiles_c = 1;  // empty: one block that reads nothing (publishes)
   const dim3 grid((unsigned)(tiles_r * tiles_c));
   if (fmt == FP8_E4M3)
-    hipLaunchKernelGGL((cast_kernel<FP8_E4M3, DERIVE>), grid, dim3(kThreads), 0, st, (const uint16_t*)x,
-                       rows, cols, tiles_c, s, out_row, out_t, margin, mu_log2);
+    hipLaunchKernelGGL((cast_kernel<FP8_E4M3, DERIVE, COUNT>), grid, dim3(kThreads), 0, st,
+                       (const uint16_t*)x, rows, cols, tiles_c, s, out_row, out_t, margin, mu_log2);
   else
-    hipLaunchKernelGGL((cast_kernel<FP8_E5M2, DERIVE>), grid, dim3(kThreads), 0, st, (const uint16_t*)x,
-                       rows, cols, tiles_c, s, out_row, out_t, margin, mu_log2);
+    hipLaunchKernelGGL((cast_kernel<FP8_E5M2, DERIVE, COUNT>), grid, dim3(kThreads), 0, st,
+                       (const uint16_t*)x, rows, cols, tiles_c, s, out_row, out_t, margin, mu_log2);
   return hipGetLastError();
 }
 
@@ -203,6 +242,11 @@ hipError_t launch_quantize(const void* x, int64_t rows, int64_t cols, int fmt, i
     return launch_cast_t<true>(x, 0, 0, fmt, s, nullptr, nullptr, margin, mu_log2, st);
   }
   return launch_cast_t<true>(x, rows, cols, fmt, s, out_row, out_t, margin, mu_log2, st);
+}
+
+hipError_t launch_wgrad_cast(const void* dw, int64_t rows, int64_t cols, fp8_scale_t* s, uint8_t* out_row,
+                             uint8_t* out_t, int margin, int mu_log2, hipStream_t st) {
+  return launch_cast_t<true, true>(dw, rows, cols, FP8_E5M2, s, out_row, out_t, margin, mu_log2, st);
 }
 
 }  // namespace fp8lin

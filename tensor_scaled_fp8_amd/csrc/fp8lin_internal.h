@@ -78,5 +78,12 @@ uint64_t next_generation();
 hipError_t launch_gemm(const uint8_t* A, int fa, const fp8_scale_t* sa, const uint8_t* B, int fb,
                        const fp8_scale_t* sb, int64_t M, int64_t N, int64_t R, void* C,
                        hipStream_t st);
+hipError_t launch_gemm_wgrad_amax(const uint8_t* A, const fp8_scale_t* sa, const uint8_t* B,
+                                  const fp8_scale_t* sb, int64_t M, int64_t N, int64_t R, void* C,
+                                  fp8_scale_t* s_out, uint64_t gen, hipStream_t st);
+// E5M2 derive-cast of a weight gradient whose amax the wgrad GEMM merged,
+// counting saturated elements into s->sat_count
+hipError_t launch_wgrad_cast(const void* dw, int64_t rows, int64_t cols, fp8_scale_t* s, uint8_t* out_row,
+                             uint8_t* out_t, int margin, int mu_log2, hipStream_t st);
 
 }  // namespace fp8lin

@@ -55,6 +55,7 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kBM = 256, kBN = 256;
 constexpr int kBK = 128;                         // k-bytes per stage (one cache line per row)
@@ -112,11 +113,15 @@ __device__ inline void block_sync_lds() {
   asm volatile("" ::: "memory");
 }
 
-template <int FA, int FB>
+// AMAX: the epilogue also takes max |C| over the bf16 values it writes and
+// merges (gen << 16) | max into s_out->gen_max (one atomic per block, as the
+// amax pass of fp8_quantize does), so a following derive-cast of C needs no
+// amax pass; block 0 also clears s_out->sat_count for that cast.
+template <int FA, int FB, bool AMAX>
 __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ B, const fp8_scale_t* __restrict__ sa,
     const fp8_scale_t* __restrict__ sb, int M, int N, int R, uint16_t* __restrict__ C, int tiles_m,
-    int tiles_n) {
+    int tiles_n, fp8_scale_t* s_out, uint64_t gen) {
   // The two stage buffers are separate LDS objects, always addressed with a
   // compile-time index, so the compiler can tell the buffer being read from
   // the one with loads in flight and does not wait for those.
@@ -352,6 +357,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
   // bytes per half buffer) is staged row-major in LDS so the block writes C
   // in whole 512-byte rows of 16-byte stores. 16-byte chunks of each LDS row
   // are XOR-swizzled by (row & 31).
+  u16x2 cmax = {0, 0};  // AMAX: running max of the 15-bit magnitudes written
   auto stage_c = [&](auto SCALE_) {
     constexpr bool SCALE = decltype(SCALE_)::value;
 #pragma unroll
@@ -372,6 +378,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
           const uint32_t p1 = __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2));
           const int chunk = 16 * wn + 4 * ni + q;
           *(lds_u32x2*)(crow + ((chunk ^ (row & 31)) << 4) + 8 * g) = (u32x2){p0, p1};
+          if constexpr (AMAX) {
+            cmax = __builtin_elementwise_max(cmax, __builtin_bit_cast(u16x2, p0 & 0x7FFF7FFFu));
+            cmax = __builtin_elementwise_max(cmax, __builtin_bit_cast(u16x2, p1 & 0x7FFF7FFFu));
+          }
         }
         // scaling path: one 32 x 32 block at a time, which bounds how many
         // accumulators are moved out of the accumulation registers at once
@@ -381,7 +391,31 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
   };
   if (fold) stage_c(std::false_type{});
   else stage_c(std::true_type{});
-  block_sync_lds();
+  if constexpr (AMAX) {
+    // rows past M and columns past N repeat valid rows / columns (clamped
+    // operand rows), so the tile max is a max over real outputs
+    uint32_t r = cmax.x > cmax.y ? cmax.x : cmax.y;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      const uint32_t o = (uint32_t)__shfl_xor((int)r, off, 64);
+      r = o > r ? o : r;
+    }
+    __shared__ uint32_t wmax[kThreads / 64];
+    if (lane == 0) wmax[w] = r;
+    block_sync_lds();
+    if (t == 0) {
+      uint32_t b = wmax[0];
+#pragma unroll
+      for (int i = 1; i < kThreads / 64; ++i) b = wmax[i] > b ? wmax[i] : b;
+      const unsigned long long v = ((unsigned long long)gen << 16) | b;
+      unsigned long long* word = (unsigned long long*)&s_out->gen_max;
+      const unsigned long long seen = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (v > seen) atomicMax(word, v);
+      if (blockIdx.x == 0) s_out->sat_count = 0u;
+    }
+  } else {
+    block_sync_lds();
+  }
 
   // Drain: lane t takes 16-byte chunk c = t % 32 of rows r0 + 8k (r0 = t / 32)
   // of each 64-row region. The LDS swizzle of row 64j + r0 + 8k is
@@ -420,12 +454,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
   else drain_all(std::false_type{});
 }
 
-template <int FA, int FB>
+template <int FA, int FB, bool AMAX = false>
 hipError_t launch_typed(const uint8_t* A, const fp8_scale_t* sa, const uint8_t* B, const fp8_scale_t* sb,
-                        int64_t M, int64_t N, int64_t R, void* C, hipStream_t st) {
+                        int64_t M, int64_t N, int64_t R, void* C, hipStream_t st, fp8_scale_t* s_out = nullptr,
+                        uint64_t gen = 0) {
   const int tiles_m = (int)((M + kBM - 1) / kBM), tiles_n = (int)((N + kBN - 1) / kBN);
-  hipLaunchKernelGGL((gemm_nt_kernel<FA, FB>), dim3(tiles_m * tiles_n), dim3(kThreads), 0, st, A, B,
-                     sa, sb, (int)M, (int)N, (int)R, (uint16_t*)C, tiles_m, tiles_n);
+  hipLaunchKernelGGL((gemm_nt_kernel<FA, FB, AMAX>), dim3(tiles_m * tiles_n), dim3(kThreads), 0, st, A, B,
+                     sa, sb, (int)M, (int)N, (int)R, (uint16_t*)C, tiles_m, tiles_n, s_out, gen);
   return hipGetLastError();
 }
 
@@ -439,6 +474,13 @@ hipError_t launch_gemm(const uint8_t* A, int fa, const fp8_scale_t* sa, const ui
   if (fa == FP8_E5M2 && fb == FP8_E4M3) return launch_typed<1, 0>(A, sa, B, sb, M, N, R, C, st);
   if (fa == FP8_E4M3 && fb == FP8_E5M2) return launch_typed<0, 1>(A, sa, B, sb, M, N, R, C, st);
   return launch_typed<1, 1>(A, sa, B, sb, M, N, R, C, st);
+}
+
+hipError_t launch_gemm_wgrad_amax(const uint8_t* A, const fp8_scale_t* sa, const uint8_t* B,
+                                  const fp8_scale_t* sb, int64_t M, int64_t N, int64_t R, void* C,
+                                  fp8_scale_t* s_out, uint64_t gen, hipStream_t st) {
+  if (M == 0 || N == 0) return hipSuccess;
+  return launch_typed<FP8_E4M3, FP8_E5M2, true>(A, sa, B, sb, M, N, R, C, st, s_out, gen);
 }
 
 }  // namespace fp8lin

@@ -31,7 +31,7 @@ def test_header_functions_all_exported():
     for n in names:
         assert hasattr(lib, n), n
         assert n in _lib.SIGNATURES, f"binding lacks {n}"
-    assert lib.fp8_abi_version() == 3
+    assert lib.fp8_abi_version() == 4
 
 
 def test_status_strings():
@@ -120,6 +120,20 @@ def test_argument_validation_without_launch():
     assert c(*args(w8t=None)) == INV
     assert c(*args(Y=_vp(ok + 2))) == INV
     assert c(*args(margin=-5000)) == INV
+    # FP8 weight gradient
+    wg = lib.fp8_wgrad_fp8
+    wargs = lambda **kw: [kw.get(k, d) for k, d in (
+        ("x8t", _vp(ok)), ("sx", _vp(ok)), ("dy8t", _vp(ok)), ("sdy", _vp(ok)), ("K", 16), ("N", 16),
+        ("M", 16), ("margin", 0), ("mu", 0), ("dW", _vp(ok)), ("s_dw", _vp(ok)), ("dw8", _vp(ok)),
+        ("dw8t", None), ("st", None))]
+    assert wg(*wargs(M=24)) == UNS
+    assert wg(*wargs(K=-16)) == INV
+    assert wg(*wargs(s_dw=None)) == INV
+    assert wg(*wargs(dw8=None)) == INV
+    assert wg(*wargs(dW=_vp(ok + 2))) == INV
+    assert wg(*wargs(dw8t=_vp(ok + 1))) == INV
+    assert wg(*wargs(mu=3000)) == INV
+    assert wg(*wargs(x8t=None)) == INV
 
 
 def test_binding_rejects_cpu_tensors():

@@ -11,7 +11,8 @@ import numpy as np
 import pytest
 
 from oracle import (E4M3, E5M2, FLAG_CLAMPED, FLAG_NONFINITE, FLAG_ZERO, amax, bf16_to_f64,
-                    cast, compute_bias, encode, f64_to_bf16_rne, fixed_record, scale_record)
+                    cast, compute_bias, encode, f64_to_bf16_rne, fixed_record, saturated_count,
+                    scale_record)
 from tests import _golden
 from workloads import f32_to_bf16_bits, random_bf16_bits
 
@@ -147,3 +148,27 @@ def test_fixed_record_matches_amax_record_of_a_tensor_at_that_bias():
     for bad in (-127, 127):
         with pytest.raises(ValueError):
             fixed_record(bad)
+
+
+@pytest.mark.parametrize("fmt,E", [(E4M3, 8), (E5M2, 15)])
+def test_saturated_count_vs_bit_threshold_and_encoder(fmt, E):
+    """The clipped-element count, exhaustively over every bf16 pattern and
+    every bias: (1) it equals the count of magnitudes above the closed-form
+    threshold pattern of max * 2^-bias (max = 1.75 * 2^E, so exponent field
+    127 + E - bias and mantissa 0x60; no finite value above the bf16 range),
+    NaN patterns excluded; (2) every counted element encodes to the +-max
+    code."""
+    allbits = np.arange(0, 0x10000, dtype=np.uint32).astype(np.uint16)
+    mag = allbits.astype(np.uint32) & 0x7FFF
+    max_code = int(encode(np.array([fmt.max_finite]), fmt)[0])
+    for b in range(-126, 127):
+        e = 127 + E - b
+        thr = (e << 7) | 0x60 if e <= 254 else 0x7F7F
+        want = int(np.count_nonzero((mag > thr) & (mag <= 0x7F80)))
+        assert saturated_count(allbits, fmt, b) == want, b
+    for b in (-60, -1, 0, 1, 7, 30):
+        x = bf16_to_f64(allbits)
+        with np.errstate(invalid="ignore", over="ignore"):
+            clipped = np.abs(np.ldexp(x, b)) > fmt.max_finite
+        q = encode(np.ldexp(x[clipped], b), fmt)
+        assert np.all((q & 0x7F) == max_code), b
