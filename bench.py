@@ -156,6 +156,7 @@ def main():
     brk = [(k, lb, b, f, hip.elapsed_ms(e0, e1)) for k, lb, b, f, e0, e1 in events]
     infer = inference_pass(tsf, torch, lin, margin, args.steps, args.warmup)
     fp8dw = fp8_dw_pass(tsf, torch, lin, margin, mu, args.steps, args.warmup)
+    o2 = adam_pass(tsf, torch, lin, margin, mu, args.steps, args.warmup)
 
     def aggregate(rows):
         agg = {}
@@ -218,6 +219,7 @@ def main():
         "frac_fp8_peak_step": round(value / PEAK_FP8_TFLOPS, 4),
         "inference": infer,
         "fp8_weight_gradient": fp8dw,
+        "o2_adam": o2,
         "input_gen_s": round(t_gen, 1),
     }
     if check is not None:
@@ -294,6 +296,39 @@ def fp8_dw_pass(tsf, torch, lin, margin, mu, steps, warmup):
     out["note"] = ("all linears' dW in E5M2 per step: wgrad GEMM + cast (fused amax) vs wgrad GEMM + "
                    f"fp8_quantize(dW); the cast moves {q_bytes} bytes per step")
     return out
+
+
+def adam_pass(tsf, torch, lin, margin, mu, steps, warmup):
+    """O2 Adam step over every weight of the layer (FP8 E4M3 first moment,
+    scaled FP16 second moment and master weights), fed by the FP8 weight
+    gradients of fp8_wgrad_fp8; the new bf16 weights are written too.
+    Algorithmic HBM bytes per parameter: two passes reading gradient (1),
+    m1 (1), m2 (2), master (2), then m1, m2, master and bf16 weights written
+    (7): 19."""
+    states = []
+    for d in lin:
+        ws = d["ws"]
+        _, dw8, _, s_dw = tsf.fp8_wgrad_fp8(ws.x8t, ws.sx, ws.dy8t, ws.sdy, margin, mu)
+        st = tsf.AdamState(d["W"])
+        states.append((st, dw8.reshape(-1), s_dw, torch.empty(st.n, dtype=torch.bfloat16, device=dw8.device)))
+    n = sum(st.n for st, _, _, _ in states)
+
+    def run():
+        for st, g8, s_g, wout in states:
+            tsf.fp8_adam_step(st, g8, s_g, 1e-4, 0.9, 0.95, 1e-8, 0.1, w_bf16=wout)
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        run()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    gbs = 19 * n / (ms * 1e-3) / 1e9
+    del states
+    return {"params": n, "ms_per_step": round(ms, 4), "GB/s": round(gbs, 1),
+            "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
+            "note": "fp8_adam_step on all weights of the layer (3 launches each), 19 algorithmic bytes/param"}
 
 
 class HipEvents:

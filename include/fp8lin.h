@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define FP8LIN_ABI_VERSION 4
+#define FP8LIN_ABI_VERSION 5
 
 typedef enum fp8_fmt {
   FP8_E4M3 = 0, /* OCP E4M3FN: weights and activations [AMAX bullet 4] */
@@ -257,6 +257,39 @@ fp8_status fp8_linear_bwd(const void* dY, int64_t M, int64_t K, int64_t N, int m
 fp8_status fp8_wgrad_fp8(const uint8_t* x8t, const fp8_scale_t* sx, const uint8_t* dy8t,
                          const fp8_scale_t* sdy, int64_t K, int64_t N, int64_t M, int margin, int mu_log2,
                          void* dW_bf16, fp8_scale_t* s_dw, uint8_t* dw8, uint8_t* dw8t, hipStream_t stream);
+
+/*
+ * O2 optimizer state [FP8LM "Proposed method", O2: precision-decoupled Adam,
+ * first moment FP8, second moment FP16, master weights FP16 with tensor
+ * scaling, 6 bytes per parameter with the FP8 gradient]. Readings where the
+ * page is silent: the first moment is E4M3 with a per-tensor record (as any
+ * FP8 tensor here); the FP16 second moment and master weights each carry a
+ * per-tensor power-of-two scale in a record (value = fp16 * scale_inv),
+ * chosen as for the FP8 path with the FP16 max 65504; the update is AdamW
+ * with bias correction in fp32; every new scale is taken just in time from
+ * the new tensor's max |value|.
+ *
+ * fp8_adam_init_master: master weights from bf16 weights: w16 [n] FP16 and
+ * its record s_w (amax rule with max 65504). The moments start as zero
+ * bytes with zeroed records (they decode as 0).
+ *
+ * fp8_adam_step: one step on n parameters, in place:
+ *   g  = dec_E5M2(g8) * s_g.scale_inv                      (e.g. fp8_wgrad_fp8)
+ *   m1 = beta1 m1 + (1 - beta1) g;  m2 = beta2 m2 + (1 - beta2) g^2
+ *   w  = w - lr ((m1 / (1 - beta1^step)) / (sqrt(m2 / (1 - beta2^step)) + eps) + weight_decay w)
+ * then m1 re-encoded in E4M3 and m2, w in FP16 with new per-tensor scales
+ * (records rewritten), and, if w_bf16 is not NULL, the new weights rounded
+ * to bf16 there (the next forward's W). Three kernel launches; a record's
+ * reduce_bits must be zero before the first call (fp8_scale_reset).
+ *   n: multiple of 16; g8, m1 [n] u8; m2, w16 [n] fp16 bits; w_bf16 [n] bf16
+ *   or NULL; all 16-B aligned device pointers. lr, eps, weight_decay finite
+ *   with eps > 0 and weight_decay >= 0; 0 <= beta < 1; step >= 1;
+ *   else FP8_ERR_INVALID.
+ */
+fp8_status fp8_adam_init_master(int64_t n, const void* w_bf16, uint16_t* w16, fp8_scale_t* s_w, hipStream_t stream);
+fp8_status fp8_adam_step(int64_t n, const uint8_t* g8, const fp8_scale_t* s_g, uint8_t* m1, fp8_scale_t* s_m1,
+                         uint16_t* m2, fp8_scale_t* s_m2, uint16_t* w16, fp8_scale_t* s_w, void* w_bf16, float lr,
+                         float beta1, float beta2, float eps, float weight_decay, int32_t step, hipStream_t stream);
 
 /* How fp8_linear_fwd_cached scales X. */
 typedef enum fp8_scaling {

@@ -33,6 +33,7 @@ from .scaling import (FLAG_NONFINITE, FLAG_ZERO, FLAG_CLAMPED, BIAS_MIN, BIAS_MA
                       amax, compute_bias, scale_record, fixed_record, saturated_count, cast)
 from .gemm import gemm_nt, gemm_nt_exact, gemm_nt_rows, tolerance
 from .linear import linear_fwd_bwd
+from . import adam
 
 __all__ = [
     "E4M3", "E5M2", "FORMATS", "Fp8Format", "decode_code", "decode_table", "encode",

@@ -32,13 +32,16 @@ SIGNATURES = {
                                       c_vp]),
     "fp8_wgrad_fp8": (c_int, [c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_int, c_int, c_vp, c_vp, c_vp, c_vp,
                               c_vp]),
+    "fp8_adam_init_master": (c_int, [c_i64, c_vp, c_vp, c_vp, c_vp]),
+    "fp8_adam_step": (c_int, [c_i64, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, ctypes.c_float,
+                              ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_int32, c_vp]),
 }
 
 FP8_E4M3, FP8_E5M2 = 0, 1
 FP8_OK, FP8_ERR_INVALID, FP8_ERR_UNSUPPORTED, FP8_ERR_HIP = 0, 1, 2, 3
 FLAG_NONFINITE, FLAG_ZERO, FLAG_CLAMPED = 1, 2, 4
 FP8_SCALING_AMAX, FP8_SCALING_FIXED = 0, 1
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 
 class LinearWs(ctypes.Structure):

@@ -4,7 +4,8 @@ every step of the computation runs in the HIP kernels of libfp8lin.so.
 
 Names follow the C entry points: fp8_amax, fp8_scale, fp8_amax_scale,
 fp8_scale_fixed, fp8_cast, fp8_gemm_nt, fp8_quantize, fp8_linear_fwd,
-fp8_linear_bwd, fp8_linear_fwd_cached, fp8_wgrad_fp8. A scaling record (fp8_scale_t, 64
+fp8_linear_bwd, fp8_linear_fwd_cached, fp8_wgrad_fp8, fp8_adam_init_master,
+fp8_adam_step. A scaling record (fp8_scale_t, 64
 bytes) is an int32 tensor of 16 words on the device."""
 from __future__ import annotations
 
@@ -328,3 +329,48 @@ class InferenceLinear(torch.nn.Module):
             self._x8 = torch.empty(x2.shape, dtype=torch.uint8, device=x2.device)
         y = fp8_linear_fwd_cached(x2, self.w8t, self.sw, self._x8, self.sx, self.margin, self.x_scaling)
         return y.reshape(*shape[:-1], y.shape[-1])
+
+
+class AdamState:
+    """O2 optimizer state of one weight tensor of n elements: first moment
+    m1 (E4M3 codes), second moment m2 and master weights w16 (FP16 bits),
+    each with its scaling record (s_m1, s_m2, s_w)."""
+
+    def __init__(self, W: torch.Tensor):
+        if W.dtype != torch.bfloat16 or not W.is_cuda:
+            raise ValueError("W must be a bf16 device tensor")
+        self.shape = tuple(W.shape)
+        self.n = W.numel()
+        dev = W.device
+        self.m1 = torch.zeros(self.n, dtype=torch.uint8, device=dev)
+        self.m2 = torch.zeros(self.n, dtype=torch.int16, device=dev)
+        self.w16 = torch.empty(self.n, dtype=torch.int16, device=dev)
+        self.scales = new_scale(3, dev)
+        self.s_m1, self.s_m2, self.s_w = self.scales[0], self.scales[1], self.scales[2]
+        self.step_count = 0
+        fp8_adam_init_master(W.reshape(-1).contiguous(), self.w16, self.s_w)
+
+
+def fp8_adam_init_master(w_bf16: torch.Tensor, w16: torch.Tensor, s_w: torch.Tensor) -> None:
+    check(load().fp8_adam_init_master(w_bf16.numel(), _dev(w_bf16, torch.bfloat16, "w_bf16"),
+                                      _dev(w16, torch.int16, "w16"), _dev(s_w, torch.int32, "s_w"),
+                                      _stream(w_bf16)), "fp8_adam_init_master")
+
+
+def fp8_adam_step(state: AdamState, g8: torch.Tensor, s_g: torch.Tensor, lr: float, beta1: float = 0.9,
+                  beta2: float = 0.95, eps: float = 1e-8, weight_decay: float = 0.0,
+                  w_bf16: Optional[torch.Tensor] = None, step: Optional[int] = None) -> Optional[torch.Tensor]:
+    """One O2 Adam step on `state` with the E5M2 gradient g8 (n codes, any
+    shape) and its record s_g; writes the new bf16 weights to w_bf16 if
+    given. `step` defaults to the state's own count + 1."""
+    if g8.numel() != state.n:
+        raise ValueError("gradient size differs from the state's")
+    t = state.step_count + 1 if step is None else int(step)
+    check(load().fp8_adam_step(state.n, _dev(g8, torch.uint8, "g8"), _dev(s_g, torch.int32, "s_g"),
+                               _dev(state.m1, torch.uint8, "m1"), _dev(state.s_m1, torch.int32, "s_m1"),
+                               _dev(state.m2, torch.int16, "m2"), _dev(state.s_m2, torch.int32, "s_m2"),
+                               _dev(state.w16, torch.int16, "w16"), _dev(state.s_w, torch.int32, "s_w"),
+                               _dev(w_bf16, torch.bfloat16, "w_bf16"), lr, beta1, beta2, eps, weight_decay, t,
+                               _stream(g8)), "fp8_adam_step")
+    state.step_count = t
+    return w_bf16

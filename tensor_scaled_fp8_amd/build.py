@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 OUT_DIR = os.path.join(PKG, "lib")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(OUT_DIR, "libfp8lin.so")
-SOURCES = ["api.hip", "amax.hip", "cast.hip", "gemm.hip"]
+SOURCES = ["api.hip", "amax.hip", "cast.hip", "gemm.hip", "adam.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

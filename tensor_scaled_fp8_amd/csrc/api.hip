@@ -3,6 +3,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <cmath>
 
 #include "fp8lin_internal.h"
 
@@ -219,6 +220,41 @@ fp8_status fp8_wgrad_fp8(const uint8_t* x8t, const fp8_scale_t* sx, const uint8_
                      : launch_amax_gen(nullptr, 0, s_dw, gen, stream);  // an empty max, so the record publishes
   if (e != hipSuccess) return FP8_ERR_HIP;
   return hip_status(launch_wgrad_cast(dW_bf16, K, N, s_dw, dw8, dw8t, margin, mu_log2, stream));
+}
+
+fp8_status fp8_adam_init_master(int64_t n, const void* w_bf16, uint16_t* w16, fp8_scale_t* s_w, hipStream_t stream) {
+  if (n < 0 || !s_w || !aligned16(s_w)) return FP8_ERR_INVALID;
+  if (n % 16) return FP8_ERR_UNSUPPORTED;
+  if (n > 0 && (!w_bf16 || !aligned16(w_bf16) || !w16 || !aligned16(w16))) return FP8_ERR_INVALID;
+  return hip_status(launch_master_init(n, (const uint16_t*)w_bf16, w16, s_w, stream));
+}
+
+fp8_status fp8_adam_step(int64_t n, const uint8_t* g8, const fp8_scale_t* s_g, uint8_t* m1, fp8_scale_t* s_m1,
+                         uint16_t* m2, fp8_scale_t* s_m2, uint16_t* w16, fp8_scale_t* s_w, void* w_bf16, float lr,
+                         float beta1, float beta2, float eps, float weight_decay, int32_t step, hipStream_t stream) {
+  if (n < 0 || step < 1) return FP8_ERR_INVALID;
+  const fp8_scale_t* recs[] = {s_g, s_m1, s_m2, s_w};
+  for (const fp8_scale_t* r : recs)
+    if (!r || !aligned16(r)) return FP8_ERR_INVALID;
+  if (!std::isfinite(lr) || !std::isfinite(eps) || !(eps > 0.0f) || !std::isfinite(weight_decay) ||
+      !(weight_decay >= 0.0f) || !(beta1 >= 0.0f && beta1 < 1.0f) || !(beta2 >= 0.0f && beta2 < 1.0f))
+    return FP8_ERR_INVALID;
+  if (n % 16) return FP8_ERR_UNSUPPORTED;
+  if (n > 0) {
+    const void* p[] = {g8, m1, m2, w16};
+    for (const void* q : p)
+      if (!q || !aligned16(q)) return FP8_ERR_INVALID;
+    if (w_bf16 && !aligned16(w_bf16)) return FP8_ERR_INVALID;
+  }
+  AdamHyper h;
+  h.lr = lr;
+  h.beta1 = beta1;
+  h.beta2 = beta2;
+  h.eps = eps;
+  h.weight_decay = weight_decay;
+  h.bc1 = (float)(1.0 / (1.0 - std::pow((double)beta1, (double)step)));
+  h.bc2 = (float)(1.0 / (1.0 - std::pow((double)beta2, (double)step)));
+  return hip_status(launch_adam(n, g8, s_g, m1, s_m1, m2, s_m2, w16, s_w, (uint16_t*)w_bf16, h, stream));
 }
 
 }  // extern "C"

@@ -53,6 +53,37 @@ __host__ __device__ inline int32_t bias_from_amax_bits(uint32_t mag, int fmt, in
   return b;
 }
 
+// The same rule for an FP16 store (max 65504 = (2 - 2^-10) * 2^15), margin 0:
+// the floor is 15 - e when the significand is <= 2 - 2^-10, else 14 - e.
+__host__ __device__ inline int32_t bias_fp16_from_amax_bits(uint32_t mag, uint32_t* flags) {
+  uint32_t f = 0;
+  int32_t b = 0;
+  if (mag >= 0x7F800000u) {
+    f = FP8_FLAG_NONFINITE;
+  } else if (mag == 0u) {
+    f = FP8_FLAG_ZERO;
+  } else {
+    const uint32_t ef = mag >> 23, mf = mag & 0x7FFFFFu;
+    int e;
+    bool above;  // significand > 2 - 2^-10
+    if (ef != 0) {
+      e = (int)ef - 127;
+      above = mf > 0x7FE000u;
+    } else {
+      const int p = 31 - __builtin_clz(mf);
+      e = p - 149;
+      above = 1024ull * mf > (2047ull << p);
+    }
+    b = 15 - e - (above ? 1 : 0);
+    if (b < kBiasMin || b > kBiasMax) {
+      f |= FP8_FLAG_CLAMPED;
+      b = b < kBiasMin ? kBiasMin : kBiasMax;
+    }
+  }
+  if (flags) *flags = f;
+  return b;
+}
+
 __host__ __device__ inline float pow2f(int32_t b) {  // 2^b for b in [-126, 127]
   union { uint32_t u; float f; } v;
   v.u = (uint32_t)(b + 127) << 23;
@@ -85,5 +116,13 @@ hipError_t launch_gemm_wgrad_amax(const uint8_t* A, const fp8_scale_t* sa, const
 // counting saturated elements into s->sat_count
 hipError_t launch_wgrad_cast(const void* dw, int64_t rows, int64_t cols, fp8_scale_t* s, uint8_t* out_row,
                              uint8_t* out_t, int margin, int mu_log2, hipStream_t st);
+
+struct AdamHyper {
+  float lr, beta1, beta2, eps, weight_decay, bc1, bc2;  // bc = 1 / (1 - beta^step)
+};
+hipError_t launch_adam(int64_t n, const uint8_t* g8, const fp8_scale_t* s_g, uint8_t* m1, fp8_scale_t* s_m1,
+                       uint16_t* m2, fp8_scale_t* s_m2, uint16_t* w, fp8_scale_t* s_w, uint16_t* w_bf16,
+                       const AdamHyper& h, hipStream_t st);
+hipError_t launch_master_init(int64_t n, const uint16_t* w_bf16, uint16_t* w, fp8_scale_t* s_w, hipStream_t st);
 
 }  // namespace fp8lin

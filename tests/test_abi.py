@@ -31,7 +31,7 @@ def test_header_functions_all_exported():
     for n in names:
         assert hasattr(lib, n), n
         assert n in _lib.SIGNATURES, f"binding lacks {n}"
-    assert lib.fp8_abi_version() == 4
+    assert lib.fp8_abi_version() == 5
 
 
 def test_status_strings():
@@ -134,6 +134,27 @@ def test_argument_validation_without_launch():
     assert wg(*wargs(dw8t=_vp(ok + 1))) == INV
     assert wg(*wargs(mu=3000)) == INV
     assert wg(*wargs(x8t=None)) == INV
+    # O2 Adam
+    ad = lib.fp8_adam_step
+    aargs = lambda **kw: [kw.get(k, d) for k, d in (
+        ("n", 64), ("g8", _vp(ok)), ("s_g", _vp(ok)), ("m1", _vp(ok)), ("s_m1", _vp(ok)), ("m2", _vp(ok)),
+        ("s_m2", _vp(ok)), ("w", _vp(ok)), ("s_w", _vp(ok)), ("wb", None), ("lr", 1e-3), ("b1", 0.9),
+        ("b2", 0.95), ("eps", 1e-8), ("wd", 0.1), ("step", 1), ("st", None))]
+    assert ad(*aargs(n=40)) == UNS
+    assert ad(*aargs(step=0)) == INV
+    assert ad(*aargs(b1=1.0)) == INV
+    assert ad(*aargs(b2=-0.1)) == INV
+    assert ad(*aargs(eps=0.0)) == INV
+    assert ad(*aargs(wd=-1.0)) == INV
+    assert ad(*aargs(lr=math.inf)) == INV
+    assert ad(*aargs(lr=math.nan)) == INV
+    assert ad(*aargs(s_m2=None)) == INV
+    assert ad(*aargs(m1=_vp(ok + 8))) == INV
+    assert ad(*aargs(wb=_vp(ok + 2))) == INV
+    im = lib.fp8_adam_init_master
+    assert im(40, _vp(ok), _vp(ok), _vp(ok), None) == UNS
+    assert im(64, None, _vp(ok), _vp(ok), None) == INV
+    assert im(64, _vp(ok), _vp(ok), None, None) == INV
 
 
 def test_binding_rejects_cpu_tensors():
