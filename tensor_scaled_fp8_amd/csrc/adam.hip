@@ -45,13 +45,17 @@ struct Vals {
 };
 
 // One element of the update, in fp32. Same instructions in both passes.
+// The square root and the reciprocal are the hardware approximations
+// (v_sqrt_f32, v_rcp_f32, about 1 ulp each): correctly rounded division and
+// square root made the pass ALU-bound, and the update needs no more than
+// fp32 accuracy.
 __device__ inline Vals adam_update(float g, float m1, float m2, float w, const AdamHyper& h) {
 #pragma clang fp contract(off)
   const float m1n = __builtin_fmaf(h.beta1, m1, (1.0f - h.beta1) * g);
   const float m2n = __builtin_fmaf(h.beta2, m2, ((1.0f - h.beta2) * g) * g);
   const float mh = m1n * h.bc1;
   const float vh = m2n * h.bc2;
-  const float step = mh / (__builtin_sqrtf(vh) + h.eps) + h.weight_decay * w;
+  const float step = mh * __builtin_amdgcn_rcpf(__builtin_amdgcn_sqrtf(vh) + h.eps) + h.weight_decay * w;
   Vals r;
   r.m1 = m1n;
   r.m2 = m2n;
