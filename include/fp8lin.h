@@ -80,13 +80,14 @@ typedef enum fp8_status {
  *   scale     2^b: multiplies the tensor before the FP8 cast [AMAX bullet 3].
  *   scale_inv 2^-b: undoes the scale after the GEMM.
  *   flags     FP8_FLAG_* bits.
- * reduce_bits and reduce_ticket are the working words of fp8_amax /
- * fp8_amax_scale (blocks merge their maxima with device-scope atomics and
- * count themselves; the last one publishes). gen_max is the working word
- * of fp8_quantize: (call generation << 16) | bf16 magnitude bits, merged by
- * atomic max, so a newer call always outranks what an older one left and
- * the word is never cleared. All three must be zero before the first call
- * on the record (allocate zeroed memory or call fp8_scale_reset once).
+ * gen_max is the working word of the amax reductions (fp8_amax,
+ * fp8_amax_scale, fp8_quantize, fp8_wgrad_fp8): (call generation << 16) |
+ * bf16 magnitude bits, merged by atomic max, so a newer call always
+ * outranks what an older one left and the word is never cleared.
+ * reduce_bits is the working word of the O2 Adam calls (fp32 magnitude
+ * bits of a running max, cleared by the call that consumes it). Both must
+ * be zero before the first call on the record (allocate zeroed memory or
+ * call fp8_scale_reset once).
  */
 typedef struct fp8_scale_t {
   float amax;
@@ -95,9 +96,9 @@ typedef struct fp8_scale_t {
   float scale_inv;
   uint32_t flags;
   uint32_t reduce_bits;   /* internal: running max of the |bf16| bit patterns */
-  uint32_t reduce_ticket; /* internal: count of blocks that have merged */
+  uint32_t reserved1;     /* unused, zero */
   uint32_t sat_count;     /* elements saturated by the last fp8_wgrad_fp8 cast */
-  uint64_t gen_max;       /* internal: generation-tagged running max (fp8_quantize) */
+  uint64_t gen_max;       /* internal: generation-tagged running max */
   uint64_t reserved2[3];
 } fp8_scale_t;
 
@@ -131,8 +132,8 @@ fp8_status fp8_amax(const void* x_bf16, int64_t n, fp8_scale_t* s_dev, hipStream
  */
 fp8_status fp8_scale(fp8_fmt fmt, int margin, int mu_log2, fp8_scale_t* s_dev, hipStream_t stream);
 
-/* a1 + a2 fused in one launch: the last reduction block writes amax, bias,
- * scale, scale_inv and flags (no separate fp8_scale call). */
+/* a1 + a2 fused: the reduction, then one publishing thread that writes
+ * amax, bias, scale, scale_inv and flags (no separate fp8_scale call). */
 fp8_status fp8_amax_scale(const void* x_bf16, int64_t n, fp8_fmt fmt, int margin, int mu_log2,
                           fp8_scale_t* s_dev, hipStream_t stream);
 

@@ -56,8 +56,8 @@ def read_scale(s: torch.Tensor) -> dict:
     f = w.view(torch.float32)
     return {"amax": float(f[0]), "bias": int(w[1]), "scale": float(f[2]),
             "scale_inv": float(f[3]), "flags": int(w[4]) & 0xFFFFFFFF,
-            "reduce_bits": int(w[5]) & 0xFFFFFFFF, "reduce_ticket": int(w[6]) & 0xFFFFFFFF,
-            "sat_count": int(w[7]) & 0xFFFFFFFF}
+            "reduce_bits": int(w[5]) & 0xFFFFFFFF, "sat_count": int(w[7]) & 0xFFFFFFFF,
+            "gen_max": (int(w[8]) & 0xFFFFFFFF) | ((int(w[9]) & 0xFFFFFFFF) << 32)}
 
 
 def fp8_scale_reset(s: torch.Tensor) -> None:

@@ -8,18 +8,18 @@
 // every finite value and NaN patterns above inf, so the integer max also
 // detects non-finite values. Two packed 16-bit maxima per dword (one VALU
 // op per two values), a wavefront max by cross-lane exchange, a block max
-// through LDS. Blocks then merge with a device-scope atomic max, skipped
-// when the target word already holds at least as much (same-address
-// atomics from many blocks serialise). Two ways to finish:
-//  * amax_kernel (fp8_amax / fp8_amax_scale, self-contained): each block
-//    waits until its max is performed, then takes a ticket; device-scope
-//    atomics are performed at one coherence point, so the block with the
-//    last ticket sees every block's max, publishes amax (and the scale) and
-//    clears the reduction word and the ticket. No L2-writeback fence.
-//  * amax_gen_kernel (fp8_quantize): merges (gen << 16) | max into a 64-bit
-//    word, gen growing with every call so older maxima never win; nothing
-//    waits inside the kernel and the word is never cleared. The cast kernel
-//    that follows derives the scale from the word and publishes the record.
+// through LDS. Blocks then merge (gen << 16) | max into the record's 64-bit
+// gen_max word with a device-scope atomic max, skipped when the word
+// already holds at least as much (same-address atomics from many blocks
+// serialise); gen grows with every call, so older maxima never win, nothing
+// waits inside the kernel and the word is never cleared. What follows on
+// the stream reads the word:
+//  * fp8_amax / fp8_amax_scale: a one-thread kernel publishes amax (and the
+//    scale). A last-block ticket in the reduction kernel itself was
+//    measured 6-8 us slower per call: every block has to wait for its merge
+//    and then for a same-address counter, which serialises 512 blocks.
+//  * fp8_quantize: the cast kernel derives the scale from the word and
+//    publishes the record.
 #include "fp8lin_internal.h"
 
 namespace fp8lin {
@@ -103,26 +103,6 @@ __device__ inline uint32_t block_max_bits(const u32x4* __restrict__ x, int64_t n
   return b;
 }
 
-__global__ __launch_bounds__(kThreads) void amax_kernel(const u32x4* __restrict__ x, int64_t n_vec,
-                                                        int64_t per_block,
-                                                        const uint16_t* __restrict__ tail,
-                                                        int tail_n, fp8_scale_t* s, int fuse, int fmt,
-                                                        int margin, int mu_log2) {
-  const uint32_t b = block_max_bits(x, n_vec, per_block, tail, tail_n);
-  if (threadIdx.x == 0) {
-    const uint32_t seen = __hip_atomic_load(&s->reduce_bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (b > seen) atomicMax(&s->reduce_bits, b);
-    // the max must have been performed before this block's ticket is taken
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    const uint32_t ticket = atomicAdd(&s->reduce_ticket, 1u);
-    if (ticket == gridDim.x - 1) {
-      const uint32_t mag = atomicExch(&s->reduce_bits, 0u);
-      atomicExch(&s->reduce_ticket, 0u);
-      write_scale(s, mag, fuse != 0, fmt, margin, mu_log2);
-    }
-  }
-}
-
 __global__ __launch_bounds__(kThreads) void amax_gen_kernel(const u32x4* __restrict__ x, int64_t n_vec,
                                                             int64_t per_block,
                                                             const uint16_t* __restrict__ tail,
@@ -134,6 +114,15 @@ __global__ __launch_bounds__(kThreads) void amax_gen_kernel(const u32x4* __restr
     const unsigned long long seen = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (v > seen) atomicMax(word, v);
   }
+}
+
+// fp8_amax / fp8_amax_scale: publish the maximum the reduction just merged
+// (the low 16 bits of gen_max; the generation tag is this call's, as no
+// other call on the record runs in between)
+__global__ void amax_publish_kernel(fp8_scale_t* s, int fuse, int fmt, int margin, int mu_log2) {
+  const unsigned long long word =
+      __hip_atomic_load((unsigned long long*)&s->gen_max, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  write_scale(s, (uint32_t)(word & 0xFFFFu), fuse != 0, fmt, margin, mu_log2);
 }
 
 __global__ void scale_kernel(fp8_scale_t* s, int fmt, int margin, int mu_log2) {
@@ -193,18 +182,18 @@ SweepGrid sweep_grid(const void* x, int64_t n) {
 }
 }  // namespace
 
-hipError_t launch_amax(const void* x, int64_t n, fp8_scale_t* s, bool fuse_scale, int fmt, int margin,
-                       int mu_log2, hipStream_t st) {
-  const SweepGrid g = sweep_grid(x, n);
-  hipLaunchKernelGGL(amax_kernel, dim3((unsigned)g.blocks), dim3(kThreads), 0, st, (const u32x4*)x, g.n_vec,
-                     g.per_block, g.tail, g.tail_n, s, fuse_scale ? 1 : 0, fmt, margin, mu_log2);
-  return hipGetLastError();
-}
-
 hipError_t launch_amax_gen(const void* x, int64_t n, fp8_scale_t* s, uint64_t gen, hipStream_t st) {
   const SweepGrid g = sweep_grid(x, n);
   hipLaunchKernelGGL(amax_gen_kernel, dim3((unsigned)g.blocks), dim3(kThreads), 0, st, (const u32x4*)x,
                      g.n_vec, g.per_block, g.tail, g.tail_n, s, gen);
+  return hipGetLastError();
+}
+
+hipError_t launch_amax(const void* x, int64_t n, fp8_scale_t* s, bool fuse_scale, int fmt, int margin,
+                       int mu_log2, hipStream_t st) {
+  const hipError_t e = launch_amax_gen(x, n, s, next_generation(), st);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(amax_publish_kernel, dim3(1), dim3(1), 0, st, s, fuse_scale ? 1 : 0, fmt, margin, mu_log2);
   return hipGetLastError();
 }
 
