@@ -4,12 +4,25 @@
         per-kernel count / total / average duration from a
         `rocprofv3 --kernel-trace --stats --output-format csv` directory.
     python -m tensor_scaled_fp8_amd.profiling traffic --fetch DIR --write DIR
-            --kernel SUBSTR --copy-bytes N [--out FILE.json]
+            --kernel SUBSTR --copy-bytes N [--command CMD] [--out FILE.json]
         HBM bytes per dispatch of the kernels whose name contains SUBSTR,
         from one `--pmc FETCH_SIZE` run and one `--pmc WRITE_SIZE` run of
         the same command. Each counter (KiB per dispatch) is scaled by what
         it reads for the plain device copy of N bytes that the benchmark
         performs (`bench.py --calibration-copy N`): factor = N / (KiB * 1024).
+    python -m tensor_scaled_fp8_amd.profiling quant-traffic --fetch DIR --write DIR
+            --copy-bytes N [--command CMD] [--out FILE.md]
+        The same counters for the cast kernels (128 x 128 tiles of 256
+        threads, so elements = work-items * 64) and the amax kernels, next
+        to the algorithmic bytes (cast: 2 read + 1 per FP8 copy written;
+        amax: 2 read).
+    python -m tensor_scaled_fp8_amd.profiling mfma DIR [--command CMD] [--out FILE.md]
+        Per GEMM dispatch shape, from one run with --pmc
+        SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_F8
+        SQ_INSTS_VALU_MFMA_MOPS_F6F4 SQ_BUSY_CYCLES: the FP8 MFMA flops
+        counted, the average shader clock over the dispatch, the MFMA busy
+        fraction at that clock and the dense FP8 peak at that clock
+        (256 CUs x 8192 flops per clock).
 """
 from __future__ import annotations
 
@@ -98,6 +111,103 @@ def traffic(fetch_dir: str, write_dir: str, kernel: str, copy_bytes: int) -> dic
     return out
 
 
+def _pmc_rows(d: str) -> dict:
+    """Dispatch id -> {"name", "grid", "ns", counter: summed value, ...}."""
+    out = {}
+    for r in csv.DictReader(open(_find(d, "counter_collection.csv"))):
+        e = out.setdefault(r["Dispatch_Id"], {"name": r["Kernel_Name"], "grid": int(r["Grid_Size"]),
+                                                "ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+        e[r["Counter_Name"]] = e.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return out
+
+
+def _copy_factor(rows: dict, counter: str, copy_bytes: int) -> float:
+    copies = [e[counter] for e in rows.values() if "copyBuffer" in e["name"] and counter in e]
+    if not copies:
+        raise RuntimeError("no copy dispatch")
+    return copy_bytes / (max(copies) * 1024.0)
+
+
+def quant_traffic_markdown(fetch_dir: str, write_dir: str, copy_bytes: int, command: str) -> str:
+    fe, wr = _pmc_rows(fetch_dir), _pmc_rows(write_dir)
+    ff, wf = _copy_factor(fe, "FETCH_SIZE", copy_bytes), _copy_factor(wr, "WRITE_SIZE", copy_bytes)
+    fk, wk = sorted(fe, key=int), sorted(wr, key=int)
+    if len(fk) != len(wk):
+        raise RuntimeError("the two runs dispatched different kernels")
+    groups = defaultdict(list)
+    pairs = list(zip(fk, wk))
+    for i, (a, b) in enumerate(pairs):
+        ea, eb = fe[a], wr[b]
+        if ea["name"] != eb["name"]:
+            raise RuntimeError("the two runs dispatched different kernels")
+        name = ea["name"]
+        fb, wb = ea["FETCH_SIZE"] * 1024 * ff, eb["WRITE_SIZE"] * 1024 * wf
+        if "cast_kernel<" in name:
+            tmpl = name[name.index("cast_kernel<"):].split(">")[0] + ">"
+            groups[(tmpl, ea["grid"] * 64)].append((fb, wb))
+        elif "amax_gen_kernel" in name:
+            # in fp8_quantize the cast of the same tensor is the next dispatch
+            nxt = fe[pairs[i + 1][0]] if i + 1 < len(pairs) else None
+            if nxt is not None and "cast_kernel<" in nxt["name"]:
+                groups[("amax_gen_kernel", nxt["grid"] * 64)].append((fb, wb))
+            else:
+                groups[("amax_gen_kernel", None)].append((fb, wb))
+    lines = ["# HBM traffic of the quantise kernels (amax and cast), GPT-7B-style layer", "",
+             "Commands (FETCH_SIZE and WRITE_SIZE in separate runs; counters scaled by a plain "
+             f"{copy_bytes}-byte device copy in the same run: fetch x{ff:.3f}, write x{wf:.3f}):", "",
+             "```", command, "```", "",
+             "Cast: elements = work-items x 64 (one 128 x 128 tile per 256 threads); algorithmic "
+             "read 2 B/element, write 1 B per FP8 copy (2 copies when the transpose is written, "
+             "template flags <fmt, derive, count>). amax: algorithmic read = 2 B/element. A write "
+             "figure below the algorithmic one means lines were still dirty in the L2 when the "
+             "dispatch ended; they reach HBM later, inside another dispatch's count.", "",
+             "| kernel | elements | dispatches | HBM read MB | alg. read MB | read/alg | HBM write MB | "
+             "write/elements (B) |", "|---|---:|---:|---:|---:|---:|---:|---:|"]
+    for (k, n), v in sorted(groups.items(), key=lambda kv: (kv[0][0], kv[0][1] or 0)):
+        if k == "amax_gen_kernel" and n is None:
+            continue  # not followed by a cast: size unknown from the counters alone
+        f = sum(x[0] for x in v) / len(v)
+        w = sum(x[1] for x in v) / len(v)
+        lines.append(f"| `{k}` | {n} | {len(v)} | {f / 1e6:.1f} | {2 * n / 1e6:.1f} | {f / (2 * n):.3f} | "
+                     f"{w / 1e6:.1f} | {w / n:.3f} |")
+    return "\n".join(lines) + "\n"
+
+
+def mfma_markdown(d: str, command: str) -> str:
+    rows = _pmc_rows(d)
+    groups = defaultdict(list)
+    for e in rows.values():
+        if "gemm_nt_kernel" not in e["name"]:
+            continue
+        tmpl = e["name"][e["name"].index("gemm_nt_kernel<"):].split(">")[0] + ">"
+        groups[(tmpl, e["grid"] // 256)].append(e)
+    lines = ["# FP8 MFMA utilisation and shader clock of the GEMM kernel, GPT-7B-style layer", "",
+             "Command:", "", "```", command, "```", "",
+             "flops = 512 x (SQ_INSTS_VALU_MFMA_MOPS_F8 + SQ_INSTS_VALU_MFMA_MOPS_F6F4); MFMA cycles = "
+             "SQ_VALU_MFMA_BUSY_CYCLES per SIMD (1024 SIMDs), which the hardware counts as 64 per "
+             "32x32x64 FP8 MFMA, so it equals flops / (1024 x 2048) when no MFMA work is wasted; "
+             "clock = SQ_BUSY_CYCLES per shader engine (32 of them) / dispatch duration (waves are "
+             "present for the whole GEMM); MFMA busy = MFMA cycles / (clock x duration); peak at "
+             "clock = 256 CUs x 8192 FP8 flops per clock x clock. Kernels run one at a time under "
+             "counter collection.", "",
+             "| kernel | tiles | dispatches | GFLOP | MFMA cycles / ideal | TFLOP/s | clock GHz | MFMA busy | "
+             "peak at clock | of 5.0 PF |", "|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|"]
+    for (k, tiles), v in sorted(groups.items()):
+        n = len(v)
+        busy = sum(e.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) for e in v) / n / 1024
+        fl = sum(512 * (e.get("SQ_INSTS_VALU_MFMA_MOPS_F8", 0.0) + e.get("SQ_INSTS_VALU_MFMA_MOPS_F6F4", 0.0))
+                 for e in v) / n
+        ns = sum(e["ns"] for e in v) / n
+        se = sum(e.get("SQ_BUSY_CYCLES", 0.0) for e in v) / n / 32
+        ghz = se / ns if se else float("nan")
+        tf = fl / ns / 1e3
+        peak = 256 * 8192 * ghz / 1e3
+        ideal = fl / (1024 * 2048)
+        lines.append(f"| `{k}` | {tiles} | {n} | {fl / 1e9:.1f} | {busy / ideal:.3f} | {tf:.0f} | {ghz:.3f} | "
+                     f"{busy / (ghz * ns):.3f} | {peak:.0f} | {tf / 5000:.3f} |")
+    return "\n".join(lines) + "\n"
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -111,12 +221,30 @@ def main():
     b.add_argument("--write", required=True)
     b.add_argument("--kernel", default="gemm_nt_kernel")
     b.add_argument("--copy-bytes", type=int, required=True)
+    b.add_argument("--command", default="")
     b.add_argument("--out")
+    c = sub.add_parser("quant-traffic")
+    c.add_argument("--fetch", required=True)
+    c.add_argument("--write", required=True)
+    c.add_argument("--copy-bytes", type=int, required=True)
+    c.add_argument("--command", default="")
+    c.add_argument("--out")
+    m = sub.add_parser("mfma")
+    m.add_argument("dir")
+    m.add_argument("--command", default="")
+    m.add_argument("--out")
     args = ap.parse_args()
     if args.cmd == "stats":
         text = stats_markdown(args.dir, args.title, args.command)
+    elif args.cmd == "quant-traffic":
+        text = quant_traffic_markdown(args.fetch, args.write, args.copy_bytes, args.command)
+    elif args.cmd == "mfma":
+        text = mfma_markdown(args.dir, args.command)
     else:
-        text = json.dumps(traffic(args.fetch, args.write, args.kernel, args.copy_bytes), indent=1) + "\n"
+        t = traffic(args.fetch, args.write, args.kernel, args.copy_bytes)
+        if args.command:
+            t["command"] = args.command
+        text = json.dumps(t, indent=1) + "\n"
     if getattr(args, "out", None):
         with open(args.out, "w") as f:
             f.write(text)
