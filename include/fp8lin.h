@@ -81,13 +81,17 @@ typedef enum fp8_status {
  *   scale_inv 2^-b: undoes the scale after the GEMM.
  *   flags     FP8_FLAG_* bits.
  * gen_max is the working word of the amax reductions (fp8_amax,
- * fp8_amax_scale, fp8_quantize, fp8_wgrad_fp8): (call generation << 16) |
- * bf16 magnitude bits, merged by atomic max, so a newer call always
- * outranks what an older one left and the word is never cleared.
+ * fp8_amax_scale, fp8_quantize, fp8_wgrad_fp8): (tag << 16) | bf16
+ * magnitude bits, merged by atomic max. A call's tag is epoch + 1, and the
+ * kernel that consumes the maximum (the cast, or the publish kernel of
+ * fp8_amax) sets epoch to that tag, so every call outranks what earlier
+ * calls left and the word is never cleared. Both words live on the device
+ * and change only inside kernels, so a captured HIP graph replays
+ * correctly (a host-side call counter would be frozen into the graph).
  * reduce_bits is the working word of the O2 Adam calls (fp32 magnitude
- * bits of a running max, cleared by the call that consumes it). Both must
- * be zero before the first call on the record (allocate zeroed memory or
- * call fp8_scale_reset once).
+ * bits of a running max, cleared by the call that consumes it). All three
+ * must be zero before the first call on the record (allocate zeroed memory
+ * or call fp8_scale_reset once).
  */
 typedef struct fp8_scale_t {
   float amax;
@@ -98,8 +102,9 @@ typedef struct fp8_scale_t {
   uint32_t reduce_bits;   /* internal: running max of the |bf16| bit patterns */
   uint32_t reserved1;     /* unused, zero */
   uint32_t sat_count;     /* elements saturated by the last fp8_wgrad_fp8 cast */
-  uint64_t gen_max;       /* internal: generation-tagged running max */
-  uint64_t reserved2[3];
+  uint64_t gen_max;       /* internal: tagged running max */
+  uint64_t epoch;         /* internal: tag of the last maximum consumed */
+  uint64_t reserved2[2];
 } fp8_scale_t;
 
 /* Human-readable name of a status. Never NULL. */

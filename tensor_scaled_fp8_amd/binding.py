@@ -57,7 +57,8 @@ def read_scale(s: torch.Tensor) -> dict:
     return {"amax": float(f[0]), "bias": int(w[1]), "scale": float(f[2]),
             "scale_inv": float(f[3]), "flags": int(w[4]) & 0xFFFFFFFF,
             "reduce_bits": int(w[5]) & 0xFFFFFFFF, "sat_count": int(w[7]) & 0xFFFFFFFF,
-            "gen_max": (int(w[8]) & 0xFFFFFFFF) | ((int(w[9]) & 0xFFFFFFFF) << 32)}
+            "gen_max": (int(w[8]) & 0xFFFFFFFF) | ((int(w[9]) & 0xFFFFFFFF) << 32),
+            "epoch": (int(w[10]) & 0xFFFFFFFF) | ((int(w[11]) & 0xFFFFFFFF) << 32)}
 
 
 def fp8_scale_reset(s: torch.Tensor) -> None:

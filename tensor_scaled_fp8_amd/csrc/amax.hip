@@ -8,12 +8,13 @@
 // every finite value and NaN patterns above inf, so the integer max also
 // detects non-finite values. Two packed 16-bit maxima per dword (one VALU
 // op per two values), a wavefront max by cross-lane exchange, a block max
-// through LDS. Blocks then merge (gen << 16) | max into the record's 64-bit
+// through LDS. Blocks then merge (tag << 16) | max into the record's 64-bit
 // gen_max word with a device-scope atomic max, skipped when the word
 // already holds at least as much (same-address atomics from many blocks
-// serialise); gen grows with every call, so older maxima never win, nothing
-// waits inside the kernel and the word is never cleared. What follows on
-// the stream reads the word:
+// serialise); tag = the record's epoch + 1 and the consumer of the maximum
+// advances epoch, so older maxima never win, nothing waits inside the
+// kernel and the word is never cleared. What follows on the stream reads
+// the word and advances epoch:
 //  * fp8_amax / fp8_amax_scale: a one-thread kernel publishes amax (and the
 //    scale). A last-block ticket in the reduction kernel itself was
 //    measured 6-8 us slower per call: every block has to wait for its merge
@@ -106,10 +107,10 @@ __device__ inline uint32_t block_max_bits(const u32x4* __restrict__ x, int64_t n
 __global__ __launch_bounds__(kThreads) void amax_gen_kernel(const u32x4* __restrict__ x, int64_t n_vec,
                                                             int64_t per_block,
                                                             const uint16_t* __restrict__ tail,
-                                                            int tail_n, fp8_scale_t* s, uint64_t gen) {
+                                                            int tail_n, fp8_scale_t* s) {
   const uint32_t b = block_max_bits(x, n_vec, per_block, tail, tail_n);
   if (threadIdx.x == 0) {
-    const unsigned long long v = ((unsigned long long)gen << 16) | b;
+    const unsigned long long v = (reduction_tag(s) << 16) | b;
     unsigned long long* word = (unsigned long long*)&s->gen_max;
     const unsigned long long seen = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (v > seen) atomicMax(word, v);
@@ -117,12 +118,12 @@ __global__ __launch_bounds__(kThreads) void amax_gen_kernel(const u32x4* __restr
 }
 
 // fp8_amax / fp8_amax_scale: publish the maximum the reduction just merged
-// (the low 16 bits of gen_max; the generation tag is this call's, as no
-// other call on the record runs in between)
+// (the low 16 bits of gen_max, whose tag is this call's) and advance epoch
 __global__ void amax_publish_kernel(fp8_scale_t* s, int fuse, int fmt, int margin, int mu_log2) {
   const unsigned long long word =
       __hip_atomic_load((unsigned long long*)&s->gen_max, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   write_scale(s, (uint32_t)(word & 0xFFFFu), fuse != 0, fmt, margin, mu_log2);
+  s->epoch = word >> 16;
 }
 
 __global__ void scale_kernel(fp8_scale_t* s, int fmt, int margin, int mu_log2) {
@@ -182,16 +183,16 @@ SweepGrid sweep_grid(const void* x, int64_t n) {
 }
 }  // namespace
 
-hipError_t launch_amax_gen(const void* x, int64_t n, fp8_scale_t* s, uint64_t gen, hipStream_t st) {
+hipError_t launch_amax_gen(const void* x, int64_t n, fp8_scale_t* s, hipStream_t st) {
   const SweepGrid g = sweep_grid(x, n);
   hipLaunchKernelGGL(amax_gen_kernel, dim3((unsigned)g.blocks), dim3(kThreads), 0, st, (const u32x4*)x,
-                     g.n_vec, g.per_block, g.tail, g.tail_n, s, gen);
+                     g.n_vec, g.per_block, g.tail, g.tail_n, s);
   return hipGetLastError();
 }
 
 hipError_t launch_amax(const void* x, int64_t n, fp8_scale_t* s, bool fuse_scale, int fmt, int margin,
                        int mu_log2, hipStream_t st) {
-  const hipError_t e = launch_amax_gen(x, n, s, next_generation(), st);
+  const hipError_t e = launch_amax_gen(x, n, s, st);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(amax_publish_kernel, dim3(1), dim3(1), 0, st, s, fuse_scale ? 1 : 0, fmt, margin, mu_log2);
   return hipGetLastError();

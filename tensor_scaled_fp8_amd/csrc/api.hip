@@ -2,19 +2,11 @@
 // launches on the caller's stream. No allocation, no host synchronisation.
 #include <string.h>
 
-#include <atomic>
 #include <cmath>
 
 #include "fp8lin_internal.h"
 
 using namespace fp8lin;
-
-namespace fp8lin {
-uint64_t next_generation() {
-  static std::atomic<uint64_t> counter{1};
-  return counter.fetch_add(1, std::memory_order_relaxed) & ((uint64_t(1) << 48) - 1);
-}
-}  // namespace fp8lin
 
 namespace {
 
@@ -111,7 +103,7 @@ fp8_status fp8_quantize(const void* x_bf16, int64_t rows, int64_t cols, fp8_fmt 
     if (out_transposed && !aligned16(out_transposed)) return FP8_ERR_INVALID;
   }
   return hip_status(launch_quantize(x_bf16, rows, cols, fmt, margin, mu_log2, s_dev, out_rowwise,
-                                    out_transposed, next_generation(), stream));
+                                    out_transposed, stream));
 }
 
 fp8_status fp8_gemm_nt(const uint8_t* A, fp8_fmt fa, const fp8_scale_t* sa, const uint8_t* B,
@@ -152,10 +144,10 @@ fp8_status fp8_linear_fwd(const void* X, const void* W, int64_t M, int64_t K, in
   if ((M * K > 0 && (!X || !aligned16(X))) || (K * N > 0 && (!W || !aligned16(W))) ||
       (M * N > 0 && (!Y || !aligned16(Y))))
     return FP8_ERR_INVALID;
-  if (launch_quantize(X, M, K, FP8_E4M3, margin, 0, ws->sx, ws->x8, ws->x8t, next_generation(), stream) !=
+  if (launch_quantize(X, M, K, FP8_E4M3, margin, 0, ws->sx, ws->x8, ws->x8t, stream) !=
       hipSuccess)
     return FP8_ERR_HIP;
-  if (launch_quantize(W, K, N, FP8_E4M3, margin, 0, ws->sw, ws->w8, ws->w8t, next_generation(), stream) !=
+  if (launch_quantize(W, K, N, FP8_E4M3, margin, 0, ws->sw, ws->w8, ws->w8t, stream) !=
       hipSuccess)
     return FP8_ERR_HIP;
   return hip_status(launch_gemm(ws->x8, FP8_E4M3, ws->sx, ws->w8t, FP8_E4M3, ws->sw, M, N, K, Y, stream));
@@ -172,7 +164,7 @@ fp8_status fp8_linear_bwd(const void* dY, int64_t M, int64_t K, int64_t N, int m
   if ((M * N > 0 && (!dY || !aligned16(dY))) || (dX && !aligned16(dX)) || (dW && !aligned16(dW)))
     return FP8_ERR_INVALID;
   hipError_t e;
-  if ((e = launch_quantize(dY, M, N, FP8_E5M2, margin, mu_log2, ws->sdy, ws->dy8, ws->dy8t, next_generation(),
+  if ((e = launch_quantize(dY, M, N, FP8_E5M2, margin, mu_log2, ws->sdy, ws->dy8, ws->dy8t,
                            stream)) != hipSuccess)
     return FP8_ERR_HIP;
   if (dX && (e = launch_gemm(ws->dy8, FP8_E5M2, ws->sdy, ws->w8, FP8_E4M3, ws->sw, M, K, N, dX, stream)) !=
@@ -196,7 +188,7 @@ fp8_status fp8_linear_fwd_cached(const void* X, int64_t M, int64_t K, int64_t N,
       (N * K > 0 && (!w8t || !aligned16(w8t))) || (M * N > 0 && (!Y || !aligned16(Y))))
     return FP8_ERR_INVALID;
   hipError_t e = x_scaling == FP8_SCALING_AMAX
-                     ? launch_quantize(X, M, K, FP8_E4M3, margin, 0, sx, x8, nullptr, next_generation(), stream)
+                     ? launch_quantize(X, M, K, FP8_E4M3, margin, 0, sx, x8, nullptr, stream)
                      : launch_cast(X, M, K, FP8_E4M3, sx, x8, nullptr, stream);
   if (e != hipSuccess) return FP8_ERR_HIP;
   return hip_status(launch_gemm(x8, FP8_E4M3, sx, w8t, FP8_E4M3, sw, M, N, K, Y, stream));
@@ -214,10 +206,9 @@ fp8_status fp8_wgrad_fp8(const uint8_t* x8t, const fp8_scale_t* sx, const uint8_
     if (dw8t && !aligned16(dw8t)) return FP8_ERR_INVALID;
     if (M > 0 && (!x8t || !aligned16(x8t) || !dy8t || !aligned16(dy8t))) return FP8_ERR_INVALID;
   }
-  const uint64_t gen = next_generation();
   hipError_t e = K > 0 && N > 0
-                     ? launch_gemm_wgrad_amax(x8t, sx, dy8t, sdy, K, N, M, dW_bf16, s_dw, gen, stream)
-                     : launch_amax_gen(nullptr, 0, s_dw, gen, stream);  // an empty max, so the record publishes
+                     ? launch_gemm_wgrad_amax(x8t, sx, dy8t, sdy, K, N, M, dW_bf16, s_dw, stream)
+                     : launch_amax_gen(nullptr, 0, s_dw, stream);  // an empty max, so the record publishes
   if (e != hipSuccess) return FP8_ERR_HIP;
   return hip_status(launch_wgrad_cast(dW_bf16, K, N, s_dw, dw8, dw8t, margin, mu_log2, stream));
 }

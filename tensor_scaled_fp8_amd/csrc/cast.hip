@@ -78,8 +78,9 @@ __device__ inline void transpose4(const uint32_t in[4], uint32_t out[4]) {
 
 // DERIVE = false: the scale comes from the record's published fields.
 // DERIVE = true (fp8_quantize): every block derives it from the record's
-// generation-tagged maximum, which the amax pass just merged, with the same
-// rule as fp8_scale; block 0 publishes the record's fields.
+// tagged maximum, which the amax pass just merged, with the same rule as
+// fp8_scale; block 0 publishes the record's fields and advances its epoch
+// to the tag it consumed.
 // COUNT (with DERIVE): also count the elements whose scaled magnitude
 // exceeds the format's max (inf included, NaN not) into s->sat_count, which
 // the kernel before this one cleared.
@@ -120,6 +121,7 @@ __global__ __launch_bounds__(kThreads) void cast_kernel(const uint16_t* __restri
       s->scale = scale;
       s->scale_inv = pow2f(-b);
       s->flags = flags;
+      s->epoch = word >> 16;  // this call's maximum is consumed
     }
   } else {
     scale = s->scale;
@@ -234,8 +236,8 @@ hipError_t launch_cast(const void* x, int64_t rows, int64_t cols, int fmt, const
 }
 
 hipError_t launch_quantize(const void* x, int64_t rows, int64_t cols, int fmt, int margin, int mu_log2,
-                           fp8_scale_t* s, uint8_t* out_row, uint8_t* out_t, uint64_t gen, hipStream_t st) {
-  hipError_t e = launch_amax_gen(x, rows * cols, s, gen, st);
+                           fp8_scale_t* s, uint8_t* out_row, uint8_t* out_t, hipStream_t st) {
+  hipError_t e = launch_amax_gen(x, rows * cols, s, st);
   if (e != hipSuccess) return e;
   if (rows == 0 || cols == 0 || (!out_row && !out_t)) {
     // nothing to cast: one block with no rows still publishes the record

@@ -84,6 +84,15 @@ __host__ __device__ inline int32_t bias_fp16_from_amax_bits(uint32_t mag, uint32
   return b;
 }
 
+// Tag under which a reduction merges this call's maximum into s->gen_max:
+// one above the record's epoch. Only the kernel that consumes the maximum
+// advances epoch (to gen_max >> 16), after the reduction kernel has
+// finished, so every block of a reduction reads the same value.
+__device__ inline unsigned long long reduction_tag(const fp8_scale_t* s) {
+  return __hip_atomic_load((const unsigned long long*)&s->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) +
+         1ull;
+}
+
 __host__ __device__ inline float pow2f(int32_t b) {  // 2^b for b in [-126, 127]
   union { uint32_t u; float f; } v;
   v.u = (uint32_t)(b + 127) << 23;
@@ -99,19 +108,17 @@ hipError_t launch_scale(fp8_scale_t* s, int fmt, int margin, int mu_log2, hipStr
 hipError_t launch_scale_fixed(fp8_scale_t* s, int32_t bias, hipStream_t st);
 hipError_t launch_cast(const void* x, int64_t rows, int64_t cols, int fmt, const fp8_scale_t* s,
                        uint8_t* out_row, uint8_t* out_t, hipStream_t st);
-hipError_t launch_amax_gen(const void* x, int64_t n, fp8_scale_t* s, uint64_t gen, hipStream_t st);
-// amax pass + cast that derives the scale (fp8_quantize); gen: a number
-// larger than any earlier call's (see next_generation)
+// tagged amax reduction into s->gen_max (see reduction_tag)
+hipError_t launch_amax_gen(const void* x, int64_t n, fp8_scale_t* s, hipStream_t st);
+// amax pass + cast that derives the scale (fp8_quantize)
 hipError_t launch_quantize(const void* x, int64_t rows, int64_t cols, int fmt, int margin, int mu_log2,
-                           fp8_scale_t* s, uint8_t* out_row, uint8_t* out_t, uint64_t gen, hipStream_t st);
-// process-wide increasing call number for fp8_quantize (48 bits used)
-uint64_t next_generation();
+                           fp8_scale_t* s, uint8_t* out_row, uint8_t* out_t, hipStream_t st);
 hipError_t launch_gemm(const uint8_t* A, int fa, const fp8_scale_t* sa, const uint8_t* B, int fb,
                        const fp8_scale_t* sb, int64_t M, int64_t N, int64_t R, void* C,
                        hipStream_t st);
 hipError_t launch_gemm_wgrad_amax(const uint8_t* A, const fp8_scale_t* sa, const uint8_t* B,
                                   const fp8_scale_t* sb, int64_t M, int64_t N, int64_t R, void* C,
-                                  fp8_scale_t* s_out, uint64_t gen, hipStream_t st);
+                                  fp8_scale_t* s_out, hipStream_t st);
 // E5M2 derive-cast of a weight gradient whose amax the wgrad GEMM merged,
 // counting saturated elements into s->sat_count
 hipError_t launch_wgrad_cast(const void* dw, int64_t rows, int64_t cols, fp8_scale_t* s, uint8_t* out_row,

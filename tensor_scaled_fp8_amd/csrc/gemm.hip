@@ -114,14 +114,15 @@ __device__ inline void block_sync_lds() {
 }
 
 // AMAX: the epilogue also takes max |C| over the bf16 values it writes and
-// merges (gen << 16) | max into s_out->gen_max (one atomic per block, as the
-// amax pass of fp8_quantize does), so a following derive-cast of C needs no
-// amax pass; block 0 also clears s_out->sat_count for that cast.
+// merges (tag << 16) | max into s_out->gen_max (one atomic per block, as the
+// amax pass of fp8_quantize does; tag = s_out->epoch + 1), so a following
+// derive-cast of C needs no amax pass; block 0 also clears
+// s_out->sat_count for that cast.
 template <int FA, int FB, bool AMAX>
 __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ B, const fp8_scale_t* __restrict__ sa,
     const fp8_scale_t* __restrict__ sb, int M, int N, int R, uint16_t* __restrict__ C, int tiles_m,
-    int tiles_n, fp8_scale_t* s_out, uint64_t gen) {
+    int tiles_n, fp8_scale_t* s_out) {
   // The two stage buffers are separate LDS objects, always addressed with a
   // compile-time index, so the compiler can tell the buffer being read from
   // the one with loads in flight and does not wait for those.
@@ -407,7 +408,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
       uint32_t b = wmax[0];
 #pragma unroll
       for (int i = 1; i < kThreads / 64; ++i) b = wmax[i] > b ? wmax[i] : b;
-      const unsigned long long v = ((unsigned long long)gen << 16) | b;
+      const unsigned long long v = (reduction_tag(s_out) << 16) | b;
       unsigned long long* word = (unsigned long long*)&s_out->gen_max;
       const unsigned long long seen = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (v > seen) atomicMax(word, v);
@@ -456,11 +457,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
 
 template <int FA, int FB, bool AMAX = false>
 hipError_t launch_typed(const uint8_t* A, const fp8_scale_t* sa, const uint8_t* B, const fp8_scale_t* sb,
-                        int64_t M, int64_t N, int64_t R, void* C, hipStream_t st, fp8_scale_t* s_out = nullptr,
-                        uint64_t gen = 0) {
+                        int64_t M, int64_t N, int64_t R, void* C, hipStream_t st, fp8_scale_t* s_out = nullptr) {
   const int tiles_m = (int)((M + kBM - 1) / kBM), tiles_n = (int)((N + kBN - 1) / kBN);
   hipLaunchKernelGGL((gemm_nt_kernel<FA, FB, AMAX>), dim3(tiles_m * tiles_n), dim3(kThreads), 0, st, A, B,
-                     sa, sb, (int)M, (int)N, (int)R, (uint16_t*)C, tiles_m, tiles_n, s_out, gen);
+                     sa, sb, (int)M, (int)N, (int)R, (uint16_t*)C, tiles_m, tiles_n, s_out);
   return hipGetLastError();
 }
 
@@ -478,9 +478,9 @@ hipError_t launch_gemm(const uint8_t* A, int fa, const fp8_scale_t* sa, const ui
 
 hipError_t launch_gemm_wgrad_amax(const uint8_t* A, const fp8_scale_t* sa, const uint8_t* B,
                                   const fp8_scale_t* sb, int64_t M, int64_t N, int64_t R, void* C,
-                                  fp8_scale_t* s_out, uint64_t gen, hipStream_t st) {
+                                  fp8_scale_t* s_out, hipStream_t st) {
   if (M == 0 || N == 0) return hipSuccess;
-  return launch_typed<FP8_E4M3, FP8_E5M2, true>(A, sa, B, sb, M, N, R, C, st, s_out, gen);
+  return launch_typed<FP8_E4M3, FP8_E5M2, true>(A, sa, B, sb, M, N, R, C, st, s_out);
 }
 
 }  // namespace fp8lin
