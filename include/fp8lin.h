@@ -8,6 +8,11 @@
  * caller owns every buffer and must keep it alive until the stream work ends.
  * All device-side scale data stays on the device, so a whole forward/backward
  * step can be enqueued (or captured in a HIP graph) with no host round trip.
+ * Calls that share a scaling record must run in stream order: two calls
+ * on one record that overlap (different streams, no event between them)
+ * race on its reduction words. Scalar arguments (margin, mu_log2, a fixed
+ * bias, the Adam hyper-parameters and step) are kernel arguments, so a
+ * captured graph replays them as captured.
  *
  * The method (sources cited by page title and section):
  *   [AMAX]  review of Perez, Zhang et al., "Training and inference of large
