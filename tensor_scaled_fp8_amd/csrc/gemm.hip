@@ -253,26 +253,22 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.0f;
 
-  // Dequantisation 2^s, s = -(ba + bb). Where it cannot take any product or
-  // FP32 partial sum out of the normal range, it is applied by the MFMA's
-  // own operand scales (E8M0 exponents 127 - ba and 127 - bb): every
-  // product and partial sum is a multiple of the smallest FP8 product
-  // (>= 2^-32) and at most R * 2^25 in size, so for -94 <= s <= 72 each value
-  // scales exactly and every FP32 rounding commutes with the scaling; the
-  // result equals accumulate-then-scale bit for bit and the epilogue skips
-  // its 256 ldexp per lane. Otherwise the operand scales are 1.0 (127) and
-  // the epilogue scales.
-  const int ba = sa->bias, bb = sb->bias;
-  const int shift = -(ba + bb);
-  const bool fold = shift >= -94 && shift <= 72;
-  const int esa = fold ? 127 - ba : 127, esb = fold ? 127 - bb : 127;
+  // Dequantisation 2^s, s = -(ba + bb), is applied to the FP32 sums in the
+  // epilogue (exact power-of-two scaling). The MFMA could apply it through
+  // its E8M0 operand scales instead, bit-identically wherever no product or
+  // partial sum leaves the normal range, and save the epilogue's 256 ldexp
+  // per lane; but the kernel runs at the chip's power limit, and the scaled
+  // instruction measured ~1 % slower over the whole GEMM than the plain one
+  // plus the ldexp. Literal zero scale operands select the plain
+  // v_mfma_f32_32x32x64_f8f6f4 (no scaling).
+  const int shift = -(sa->bias + sb->bias);
   auto mfma_all = [&](const Frags& f) {
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
       for (int ni = 0; ni < 4; ++ni)
         acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[ni], f.a[mi], acc[mi][ni], FB, FA,
-                                                                       0, esb, 0, esa);
+                                                                       0, 0, 0, 0);
   };
 
   // Software pipeline. Stage s lives in buffer s % 2; its two MFMA steps use
@@ -358,45 +354,36 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
   wait_vmcnt<0>();
   block_sync_lds();
 
-  // ---- epilogue: 2^s if not folded into the MFMAs (exact power-of-two
-  // scaling), bf16 RNE, then the 256 x 256 bf16 tile (128 KB: 64 rows of 512
-  // bytes per half buffer) is staged row-major in LDS so the block writes C
-  // in whole 512-byte rows of 16-byte stores. 16-byte chunks of each LDS row
-  // are XOR-swizzled by (row & 31).
+  // ---- epilogue: 2^s (exact power-of-two scaling), bf16 RNE, then the
+  // 256 x 256 bf16 tile (128 KB: 64 rows of 512 bytes per half buffer) is
+  // staged row-major in LDS so the block writes C in whole 512-byte rows of
+  // 16-byte stores. 16-byte chunks of each LDS row are XOR-swizzled by
+  // (row & 31).
   u16x2 cmax = {0, 0};  // AMAX: running max of the 15-bit magnitudes written
-  auto stage_c = [&](auto SCALE_) {
-    constexpr bool SCALE = decltype(SCALE_)::value;
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
-      const int row = 128 * wm + 32 * mi + frow;
-      lds_u8* crow = (wm ? slot(S1{}) : slot(S0{})) + (mi >> 1) * (kStageBytes / 2) + (row & 63) * 512;
+  for (int mi = 0; mi < 4; ++mi) {
+    const int row = 128 * wm + 32 * mi + frow;
+    lds_u8* crow = (wm ? slot(S1{}) : slot(S0{})) + (mi >> 1) * (kStageBytes / 2) + (row & 63) * 512;
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni) {
+    for (int ni = 0; ni < 4; ++ni) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          f32x2 lo = {acc[mi][ni][4 * q + 0], acc[mi][ni][4 * q + 1]};
-          f32x2 hi = {acc[mi][ni][4 * q + 2], acc[mi][ni][4 * q + 3]};
-          if constexpr (SCALE) {
-            lo = (f32x2){ldexpf(lo.x, shift), ldexpf(lo.y, shift)};
-            hi = (f32x2){ldexpf(hi.x, shift), ldexpf(hi.y, shift)};
-          }
-          const uint32_t p0 = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2));
-          const uint32_t p1 = __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2));
-          const int chunk = 16 * wn + 4 * ni + q;
-          *(lds_u32x2*)(crow + ((chunk ^ (row & 31)) << 4) + 8 * g) = (u32x2){p0, p1};
-          if constexpr (AMAX) {
-            cmax = __builtin_elementwise_max(cmax, __builtin_bit_cast(u16x2, p0 & 0x7FFF7FFFu));
-            cmax = __builtin_elementwise_max(cmax, __builtin_bit_cast(u16x2, p1 & 0x7FFF7FFFu));
-          }
+      for (int q = 0; q < 4; ++q) {
+        const f32x2 lo = {ldexpf(acc[mi][ni][4 * q + 0], shift), ldexpf(acc[mi][ni][4 * q + 1], shift)};
+        const f32x2 hi = {ldexpf(acc[mi][ni][4 * q + 2], shift), ldexpf(acc[mi][ni][4 * q + 3], shift)};
+        const uint32_t p0 = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2));
+        const uint32_t p1 = __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2));
+        const int chunk = 16 * wn + 4 * ni + q;
+        *(lds_u32x2*)(crow + ((chunk ^ (row & 31)) << 4) + 8 * g) = (u32x2){p0, p1};
+        if constexpr (AMAX) {
+          cmax = __builtin_elementwise_max(cmax, __builtin_bit_cast(u16x2, p0 & 0x7FFF7FFFu));
+          cmax = __builtin_elementwise_max(cmax, __builtin_bit_cast(u16x2, p1 & 0x7FFF7FFFu));
         }
-        // scaling path: one 32 x 32 block at a time, which bounds how many
-        // accumulators are moved out of the accumulation registers at once
-        if constexpr (SCALE) __builtin_amdgcn_sched_barrier(0);
       }
+      // one 32 x 32 block at a time, which bounds how many accumulators
+      // are moved out of the accumulation registers at once
+      __builtin_amdgcn_sched_barrier(0);
     }
-  };
-  if (fold) stage_c(std::false_type{});
-  else stage_c(std::true_type{});
+  }
   if constexpr (AMAX) {
     // rows past M and columns past N repeat valid rows / columns (clamped
     // operand rows), so the tile max is a max over real outputs
