@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define FP8LIN_ABI_VERSION 5
+#define FP8LIN_ABI_VERSION 6
 
 typedef enum fp8_fmt {
   FP8_E4M3 = 0, /* OCP E4M3FN: weights and activations [AMAX bullet 4] */
@@ -210,12 +210,38 @@ fp8_status fp8_gemm_nt(const uint8_t* A, fp8_fmt fa, const fp8_scale_t* sa, cons
                        fp8_fmt fb, const fp8_scale_t* sb, int64_t M, int64_t N, int64_t R,
                        void* C_bf16, hipStream_t stream);
 
+/* How a GEMM operand is stored. */
+typedef enum {
+  FP8_OPERAND_ROWS = 0, /* one row per output index, reduction contiguous: A [M,R], B [N,R] */
+  FP8_OPERAND_COLS = 1  /* reduction-major: A [R,M], B [R,N] (the row-major FP8 copy of the
+                           tensor that was cast, read transposed) */
+} fp8_layout;
+
+/*
+ * a4-a6 - the same GEMM with either operand in either layout (same
+ * arguments, rules and result as fp8_gemm_nt, which is la = lb = ROWS):
+ *   C[i, j] = bf16_rne( 2^-(sa.bias + sb.bias) * sum_r A(i, r) * B(j, r) )
+ * with A(i, r) = A[i, r] (ROWS) or A[r, i] (COLS), B likewise. With COLS the
+ * transposed FP8 copies are not needed:
+ *   Forward:  Y  = gemm(A = x8 [M,K] ROWS,  B = w8 [K,N] COLS)
+ *   Dgrad:    dX = gemm(A = dy8 [M,N] ROWS, B = w8 [K,N] ROWS)
+ *   Wgrad:    dW = gemm(A = x8 [M,K] COLS,  B = dy8 [M,N] COLS)
+ * la, lb outside fp8_layout -> FP8_ERR_INVALID.
+ */
+fp8_status fp8_gemm(const uint8_t* A, fp8_fmt fa, fp8_layout la, const fp8_scale_t* sa, const uint8_t* B,
+                    fp8_fmt fb, fp8_layout lb, const fp8_scale_t* sb, int64_t M, int64_t N, int64_t R,
+                    void* C_bf16, hipStream_t stream);
+
 /*
  * Workspace of one FP8 linear: device pointers owned by the caller.
- *   x8 [M,K], x8t [K,M], w8 [K,N], w8t [N,K], dy8 [M,N], dy8t [N,M]  (u8)
+ *   x8 [M,K], w8 [K,N], dy8 [M,N] (u8, row-major FP8 copies): required.
+ *   x8t [K,M], w8t [N,K], dy8t [N,M] (transposed copies): optional, NULL
+ *   to skip. The GEMMs read only the row-major copies (reduction-major
+ *   where needed, see fp8_gemm); a transposed copy is written when its
+ *   pointer is set, for callers that want it.
  *   sx, sw, sdy: zero-initialised scaling records (see fp8_scale_t).
- * The forward fills x8, x8t, w8, w8t, sx, sw; the backward reads them and
- * fills dy8, dy8t, sdy.
+ * The forward fills x8, w8, sx, sw (and x8t, w8t if set); the backward
+ * reads them and fills dy8, sdy (and dy8t if set).
  */
 typedef struct fp8_linear_ws {
   uint8_t* x8;
@@ -231,7 +257,7 @@ typedef struct fp8_linear_ws {
 
 /*
  * Forward of one linear, Y = X W: fp8_quantize of X and W (E4M3), then the
- * forward GEMM.
+ * forward GEMM gemm(x8 ROWS, w8 COLS).
  *   X [M,K] bf16, W [K,N] bf16 (in x out), Y [M,N] bf16; device, 16-B aligned.
  *   M, K, N multiples of 16, every FP8 operand below 4 GiB. ws: host struct
  *   of device pointers (above).
@@ -241,8 +267,8 @@ fp8_status fp8_linear_fwd(const void* X, const void* W, int64_t M, int64_t K, in
 
 /*
  * Backward of one linear: fp8_quantize of dY (E5M2, with mu = 2^mu_log2),
- * then dX = dY W^T and dW = X^T dY from the FP8 copies the forward left
- * in ws.
+ * then dX = dY W^T = gemm(dy8 ROWS, w8 ROWS) and dW = X^T dY =
+ * gemm(x8 COLS, dy8 COLS) from the FP8 copies the forward left in ws.
  *   dY [M,N] bf16; dX [M,K] bf16 or NULL to skip; dW [K,N] bf16 or NULL to skip.
  */
 fp8_status fp8_linear_bwd(const void* dY, int64_t M, int64_t K, int64_t N, int margin, int mu_log2,
@@ -258,16 +284,20 @@ fp8_status fp8_linear_bwd(const void* dY, int64_t M, int64_t K, int64_t N, int m
  * dW again for its amax. s_dw->sat_count is set to the number of elements
  * whose scaled magnitude exceeded the E5M2 max (clipped to it; inf counts,
  * NaN does not): the signal a mu auto-scaling policy needs.
- *   x8t [K,M] E4M3 with sx, dy8t [N,M] E5M2 with sdy: as for the wgrad GEMM.
+ *   x8 (E4M3, record sx) and dy8 (E5M2, record sdy), each in either
+ *   layout, as operands A and B of fp8_gemm: lx = ROWS for X^T [K,M],
+ *   COLS for the row-major X [M,K]; ldy = ROWS for dY^T [N,M], COLS for
+ *   dY [M,N]. A layout outside fp8_layout -> FP8_ERR_INVALID.
  *   dW_bf16 [K,N] bf16: written (and read back by the cast).
  *   dw8 [K,N] u8 E5M2: written. dw8t [N,K] u8: written, or NULL to skip.
  *   s_dw: dW's record (written; zero its internal words once, as for any
  *   record). K, N, M multiples of 16, operands below 4 GiB; device
  *   pointers 16-B aligned.
  */
-fp8_status fp8_wgrad_fp8(const uint8_t* x8t, const fp8_scale_t* sx, const uint8_t* dy8t,
-                         const fp8_scale_t* sdy, int64_t K, int64_t N, int64_t M, int margin, int mu_log2,
-                         void* dW_bf16, fp8_scale_t* s_dw, uint8_t* dw8, uint8_t* dw8t, hipStream_t stream);
+fp8_status fp8_wgrad_fp8(const uint8_t* x8, fp8_layout lx, const fp8_scale_t* sx, const uint8_t* dy8,
+                         fp8_layout ldy, const fp8_scale_t* sdy, int64_t K, int64_t N, int64_t M, int margin,
+                         int mu_log2, void* dW_bf16, fp8_scale_t* s_dw, uint8_t* dw8, uint8_t* dw8t,
+                         hipStream_t stream);
 
 /*
  * O2 optimizer state [FP8LM "Proposed method", O2: precision-decoupled Adam,

@@ -26,22 +26,24 @@ SIGNATURES = {
     "fp8_scale_fixed": (c_int, [c_vp, ctypes.c_int32, c_vp]),
     "fp8_cast": (c_int, [c_vp, c_i64, c_i64, c_int, c_vp, c_vp, c_vp, c_vp]),
     "fp8_gemm_nt": (c_int, [c_vp, c_int, c_vp, c_vp, c_int, c_vp, c_i64, c_i64, c_i64, c_vp, c_vp]),
+    "fp8_gemm": (c_int, [c_vp, c_int, c_int, c_vp, c_vp, c_int, c_int, c_vp, c_i64, c_i64, c_i64, c_vp, c_vp]),
     "fp8_linear_fwd": (c_int, [c_vp, c_vp, c_i64, c_i64, c_i64, c_int, c_vp, c_vp, c_vp]),
     "fp8_linear_bwd": (c_int, [c_vp, c_i64, c_i64, c_i64, c_int, c_int, c_vp, c_vp, c_vp, c_vp]),
     "fp8_linear_fwd_cached": (c_int, [c_vp, c_i64, c_i64, c_i64, c_int, c_int, c_vp, c_vp, c_vp, c_vp, c_vp,
                                       c_vp]),
-    "fp8_wgrad_fp8": (c_int, [c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_int, c_int, c_vp, c_vp, c_vp, c_vp,
-                              c_vp]),
+    "fp8_wgrad_fp8": (c_int, [c_vp, c_int, c_vp, c_vp, c_int, c_vp, c_i64, c_i64, c_i64, c_int, c_int, c_vp, c_vp,
+                              c_vp, c_vp, c_vp]),
     "fp8_adam_init_master": (c_int, [c_i64, c_vp, c_vp, c_vp, c_vp]),
     "fp8_adam_step": (c_int, [c_i64, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, ctypes.c_float,
                               ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_int32, c_vp]),
 }
 
 FP8_E4M3, FP8_E5M2 = 0, 1
+FP8_OPERAND_ROWS, FP8_OPERAND_COLS = 0, 1
 FP8_OK, FP8_ERR_INVALID, FP8_ERR_UNSUPPORTED, FP8_ERR_HIP = 0, 1, 2, 3
 FLAG_NONFINITE, FLAG_ZERO, FLAG_CLAMPED = 1, 2, 4
 FP8_SCALING_AMAX, FP8_SCALING_FIXED = 0, 1
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 
 class LinearWs(ctypes.Structure):

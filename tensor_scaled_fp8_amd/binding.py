@@ -3,7 +3,7 @@ marshalling only. Torch supplies device memory and the current HIP stream;
 every step of the computation runs in the HIP kernels of libfp8lin.so.
 
 Names follow the C entry points: fp8_amax, fp8_scale, fp8_amax_scale,
-fp8_scale_fixed, fp8_cast, fp8_gemm_nt, fp8_quantize, fp8_linear_fwd,
+fp8_scale_fixed, fp8_cast, fp8_gemm_nt, fp8_gemm, fp8_quantize, fp8_linear_fwd,
 fp8_linear_bwd, fp8_linear_fwd_cached, fp8_wgrad_fp8, fp8_adam_init_master,
 fp8_adam_step. A scaling record (fp8_scale_t, 64
 bytes) is an int32 tensor of 16 words on the device."""
@@ -15,7 +15,8 @@ from typing import Optional
 import torch
 
 from . import _lib
-from ._lib import FP8_E4M3, FP8_E5M2, FP8_SCALING_AMAX, FP8_SCALING_FIXED, LinearWs, check, load
+from ._lib import (FP8_E4M3, FP8_E5M2, FP8_OPERAND_COLS, FP8_OPERAND_ROWS, FP8_SCALING_AMAX, FP8_SCALING_FIXED,
+                   LinearWs, check, load)
 
 SCALE_WORDS = 16         # sizeof(fp8_scale_t) / 4
 SCALINGS = {"amax": FP8_SCALING_AMAX, "fixed": FP8_SCALING_FIXED}
@@ -144,23 +145,51 @@ def fp8_gemm_nt(a: torch.Tensor, fa, sa: torch.Tensor, b: torch.Tensor, fb, sb: 
     return out
 
 
-class LinearWorkspace:
-    """Device buffers of one FP8 linear (FP8 copies of X, W, dY in both
-    layouts and the three scaling records)."""
+LAYOUTS = {"rows": FP8_OPERAND_ROWS, "cols": FP8_OPERAND_COLS}
 
-    def __init__(self, M: int, K: int, N: int, device="cuda"):
+
+def fp8_gemm(a: torch.Tensor, fa, sa: torch.Tensor, b: torch.Tensor, fb, sb: torch.Tensor,
+             out: Optional[torch.Tensor] = None, a_layout: str = "rows", b_layout: str = "rows") -> torch.Tensor:
+    """C[M, N] (bf16) = 2^-(bias_a + bias_b) * sum_r A(i, r) B(j, r) on FP8 codes,
+    each operand either "rows" (A [M, R], B [N, R]) or "cols" (A [R, M], B [R, N])."""
+    if a_layout not in LAYOUTS or b_layout not in LAYOUTS:
+        raise ValueError("layouts are 'rows' or 'cols'")
+    if a.dim() != 2 or b.dim() != 2:
+        raise ValueError("A and B must be 2-D")
+    M, Ra = (a.shape[1], a.shape[0]) if a_layout == "cols" else tuple(a.shape)
+    N, Rb = (b.shape[1], b.shape[0]) if b_layout == "cols" else tuple(b.shape)
+    if Ra != Rb:
+        raise ValueError(f"reduction mismatch: A {tuple(a.shape)} ({a_layout}), B {tuple(b.shape)} ({b_layout})")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    if tuple(out.shape) != (M, N):
+        raise ValueError("out has the wrong shape")
+    check(load().fp8_gemm(_dev(a, torch.uint8, "A"), _fmt(fa), LAYOUTS[a_layout], _dev(sa, torch.int32, "sa"),
+                          _dev(b, torch.uint8, "B"), _fmt(fb), LAYOUTS[b_layout], _dev(sb, torch.int32, "sb"),
+                          M, N, Ra, _dev(out, torch.bfloat16, "out"), _stream(a)), "fp8_gemm")
+    return out
+
+
+class LinearWorkspace:
+    """Device buffers of one FP8 linear: the row-major FP8 copies of X, W
+    and dY, the three scaling records and, with transposed=True, the
+    transposed FP8 copies as well (the linear entry points then also write
+    them; their GEMMs never need them)."""
+
+    def __init__(self, M: int, K: int, N: int, device="cuda", transposed: bool = False):
         u8 = dict(dtype=torch.uint8, device=device)
         self.M, self.K, self.N = M, K, N
         self.x8 = torch.empty((M, K), **u8)
-        self.x8t = torch.empty((K, M), **u8)
         self.w8 = torch.empty((K, N), **u8)
-        self.w8t = torch.empty((N, K), **u8)
         self.dy8 = torch.empty((M, N), **u8)
-        self.dy8t = torch.empty((N, M), **u8)
+        self.x8t = torch.empty((K, M), **u8) if transposed else None
+        self.w8t = torch.empty((N, K), **u8) if transposed else None
+        self.dy8t = torch.empty((N, M), **u8) if transposed else None
         self.scales = new_scale(3, device)
         self.sx, self.sw, self.sdy = self.scales[0], self.scales[1], self.scales[2]
-        self.c = LinearWs(*[t.data_ptr() for t in (self.x8, self.x8t, self.w8, self.w8t, self.dy8,
-                                                    self.dy8t, self.sx, self.sw, self.sdy)])
+        self.c = LinearWs(*[None if t is None else t.data_ptr()
+                            for t in (self.x8, self.x8t, self.w8, self.w8t, self.dy8, self.dy8t, self.sx,
+                                      self.sw, self.sdy)])
 
 
 def fp8_linear_fwd(X: torch.Tensor, W: torch.Tensor, ws: LinearWorkspace, margin: int = 0,
@@ -237,19 +266,25 @@ class Linear(torch.nn.Module):
         return linear(x, self.weight, self.margin, self.mu_log2)
 
 
-def fp8_wgrad_fp8(x8t: torch.Tensor, sx: torch.Tensor, dy8t: torch.Tensor, sdy: torch.Tensor,
+def fp8_wgrad_fp8(x8: torch.Tensor, sx: torch.Tensor, dy8: torch.Tensor, sdy: torch.Tensor,
                   margin: int = 0, mu_log2: int = 0, dW: Optional[torch.Tensor] = None,
                   s_dw: Optional[torch.Tensor] = None, dw8: Optional[torch.Tensor] = None,
-                  dw8t: Optional[torch.Tensor] = None, transposed: bool = False):
+                  dw8t: Optional[torch.Tensor] = None, transposed: bool = False, x_layout: str = "rows",
+                  dy_layout: str = "rows"):
     """FP8 weight gradient: dW = X^T dY (bf16, the GEMM's epilogue also
     takes max |dW|), then dW in E5M2 with the bias from that amax, the margin
-    and mu = 2^mu_log2. x8t [K, M], dy8t [N, M]. Returns (dW [K, N] bf16,
+    and mu = 2^mu_log2. x8: X^T [K, M] ("rows") or X [M, K] ("cols"); dy8:
+    dY^T [N, M] ("rows") or dY [M, N] ("cols"). Returns (dW [K, N] bf16,
     dw8 [K, N] u8, dw8t [N, K] u8 or None, s_dw)."""
-    if x8t.dim() != 2 or dy8t.dim() != 2 or x8t.shape[1] != dy8t.shape[1]:
-        raise ValueError(f"shape mismatch: x8t {tuple(x8t.shape)}, dy8t {tuple(dy8t.shape)}")
-    K, M = x8t.shape
-    N = dy8t.shape[0]
-    dev = x8t.device
+    if x_layout not in LAYOUTS or dy_layout not in LAYOUTS:
+        raise ValueError("layouts are 'rows' or 'cols'")
+    if x8.dim() != 2 or dy8.dim() != 2:
+        raise ValueError("x8 and dy8 must be 2-D")
+    K, M = (x8.shape[1], x8.shape[0]) if x_layout == "cols" else tuple(x8.shape)
+    N, M2 = (dy8.shape[1], dy8.shape[0]) if dy_layout == "cols" else tuple(dy8.shape)
+    if M != M2:
+        raise ValueError(f"shape mismatch: x8 {tuple(x8.shape)} ({x_layout}), dy8 {tuple(dy8.shape)} ({dy_layout})")
+    dev = x8.device
     if dW is None:
         dW = torch.empty((K, N), dtype=torch.bfloat16, device=dev)
     if dw8 is None:
@@ -258,11 +293,11 @@ def fp8_wgrad_fp8(x8t: torch.Tensor, sx: torch.Tensor, dy8t: torch.Tensor, sdy: 
         dw8t = torch.empty((N, K), dtype=torch.uint8, device=dev)
     if s_dw is None:
         s_dw = new_scale(1, dev)[0]
-    check(load().fp8_wgrad_fp8(_dev(x8t, torch.uint8, "x8t"), _dev(sx, torch.int32, "sx"),
-                               _dev(dy8t, torch.uint8, "dy8t"), _dev(sdy, torch.int32, "sdy"), K, N, M,
-                               margin, mu_log2, _dev(dW, torch.bfloat16, "dW"), _dev(s_dw, torch.int32, "s_dw"),
-                               _dev(dw8, torch.uint8, "dw8"), _dev(dw8t, torch.uint8, "dw8t"), _stream(x8t)),
-          "fp8_wgrad_fp8")
+    check(load().fp8_wgrad_fp8(_dev(x8, torch.uint8, "x8"), LAYOUTS[x_layout], _dev(sx, torch.int32, "sx"),
+                               _dev(dy8, torch.uint8, "dy8"), LAYOUTS[dy_layout], _dev(sdy, torch.int32, "sdy"),
+                               K, N, M, margin, mu_log2, _dev(dW, torch.bfloat16, "dW"),
+                               _dev(s_dw, torch.int32, "s_dw"), _dev(dw8, torch.uint8, "dw8"),
+                               _dev(dw8t, torch.uint8, "dw8t"), _stream(x8)), "fp8_wgrad_fp8")
     return dW, dw8, dw8t, s_dw
 
 

@@ -106,10 +106,12 @@ fp8_status fp8_quantize(const void* x_bf16, int64_t rows, int64_t cols, fp8_fmt 
                                     out_transposed, stream));
 }
 
-fp8_status fp8_gemm_nt(const uint8_t* A, fp8_fmt fa, const fp8_scale_t* sa, const uint8_t* B,
-                       fp8_fmt fb, const fp8_scale_t* sb, int64_t M, int64_t N, int64_t R,
-                       void* C_bf16, hipStream_t stream) {
+fp8_status fp8_gemm(const uint8_t* A, fp8_fmt fa, fp8_layout la, const fp8_scale_t* sa, const uint8_t* B,
+                    fp8_fmt fb, fp8_layout lb, const fp8_scale_t* sb, int64_t M, int64_t N, int64_t R,
+                    void* C_bf16, hipStream_t stream) {
   if (M < 0 || N < 0 || R < 0 || !fmt_ok(fa) || !fmt_ok(fb)) return FP8_ERR_INVALID;
+  if ((la != FP8_OPERAND_ROWS && la != FP8_OPERAND_COLS) || (lb != FP8_OPERAND_ROWS && lb != FP8_OPERAND_COLS))
+    return FP8_ERR_INVALID;
   if (!sa || !sb || !aligned16(sa) || !aligned16(sb)) return FP8_ERR_INVALID;
   if (M % 16 || N % 16 || R % 16 || M >= kMaxDim || N >= kMaxDim || R >= kMaxDim || !gemm_fits(M, N, R))
     return FP8_ERR_UNSUPPORTED;
@@ -117,19 +119,27 @@ fp8_status fp8_gemm_nt(const uint8_t* A, fp8_fmt fa, const fp8_scale_t* sa, cons
     if (!C_bf16 || !aligned16(C_bf16)) return FP8_ERR_INVALID;
     if (R > 0 && (!A || !B || !aligned16(A) || !aligned16(B))) return FP8_ERR_INVALID;
   }
-  return hip_status(launch_gemm(A, fa, sa, B, fb, sb, M, N, R, C_bf16, stream));
+  return hip_status(launch_gemm(A, fa, la == FP8_OPERAND_COLS, sa, B, fb, lb == FP8_OPERAND_COLS, sb, M, N, R,
+                                C_bf16, stream));
 }
 
+fp8_status fp8_gemm_nt(const uint8_t* A, fp8_fmt fa, const fp8_scale_t* sa, const uint8_t* B,
+                       fp8_fmt fb, const fp8_scale_t* sb, int64_t M, int64_t N, int64_t R,
+                       void* C_bf16, hipStream_t stream) {
+  return fp8_gemm(A, fa, FP8_OPERAND_ROWS, sa, B, fb, FP8_OPERAND_ROWS, sb, M, N, R, C_bf16, stream);
+}
+
+// required: x8, w8, sx, sw (and dy8, sdy for the backward); optional
+// (NULL or aligned): the transposed copies x8t, w8t, dy8t
 static fp8_status check_ws(const fp8_linear_ws* ws, bool fwd) {
   if (!ws) return FP8_ERR_INVALID;
-  const void* p[] = {ws->x8, ws->x8t, ws->w8, ws->w8t, ws->sx, ws->sw};
+  const void* p[] = {ws->x8, ws->w8, ws->sx, ws->sw, fwd ? (const void*)ws->x8 : (const void*)ws->dy8,
+                     fwd ? (const void*)ws->x8 : (const void*)ws->sdy};
   for (const void* q : p)
     if (!q || !aligned16(q)) return FP8_ERR_INVALID;
-  if (!fwd) {
-    const void* r[] = {ws->dy8, ws->dy8t, ws->sdy};
-    for (const void* q : r)
-      if (!q || !aligned16(q)) return FP8_ERR_INVALID;
-  }
+  const void* o[] = {ws->x8t, ws->w8t, ws->dy8t};
+  for (const void* q : o)
+    if (q && !aligned16(q)) return FP8_ERR_INVALID;
   return FP8_OK;
 }
 
@@ -150,7 +160,8 @@ fp8_status fp8_linear_fwd(const void* X, const void* W, int64_t M, int64_t K, in
   if (launch_quantize(W, K, N, FP8_E4M3, margin, 0, ws->sw, ws->w8, ws->w8t, stream) !=
       hipSuccess)
     return FP8_ERR_HIP;
-  return hip_status(launch_gemm(ws->x8, FP8_E4M3, ws->sx, ws->w8t, FP8_E4M3, ws->sw, M, N, K, Y, stream));
+  // Y[m, n] = sum_k x8[m, k] w8[k, n]: w8 read reduction-major
+  return hip_status(launch_gemm(ws->x8, FP8_E4M3, false, ws->sx, ws->w8, FP8_E4M3, true, ws->sw, M, N, K, Y, stream));
 }
 
 fp8_status fp8_linear_bwd(const void* dY, int64_t M, int64_t K, int64_t N, int margin, int mu_log2,
@@ -167,10 +178,11 @@ fp8_status fp8_linear_bwd(const void* dY, int64_t M, int64_t K, int64_t N, int m
   if ((e = launch_quantize(dY, M, N, FP8_E5M2, margin, mu_log2, ws->sdy, ws->dy8, ws->dy8t,
                            stream)) != hipSuccess)
     return FP8_ERR_HIP;
-  if (dX && (e = launch_gemm(ws->dy8, FP8_E5M2, ws->sdy, ws->w8, FP8_E4M3, ws->sw, M, K, N, dX, stream)) !=
+  if (dX && (e = launch_gemm(ws->dy8, FP8_E5M2, false, ws->sdy, ws->w8, FP8_E4M3, false, ws->sw, M, K, N, dX, stream)) !=
                 hipSuccess)
     return FP8_ERR_HIP;
-  if (dW && (e = launch_gemm(ws->x8t, FP8_E4M3, ws->sx, ws->dy8t, FP8_E5M2, ws->sdy, K, N, M, dW, stream)) !=
+  // dW[k, n] = sum_m x8[m, k] dy8[m, n]: both read reduction-major
+  if (dW && (e = launch_gemm(ws->x8, FP8_E4M3, true, ws->sx, ws->dy8, FP8_E5M2, true, ws->sdy, K, N, M, dW, stream)) !=
                 hipSuccess)
     return FP8_ERR_HIP;
   return FP8_OK;
@@ -191,23 +203,27 @@ fp8_status fp8_linear_fwd_cached(const void* X, int64_t M, int64_t K, int64_t N,
                      ? launch_quantize(X, M, K, FP8_E4M3, margin, 0, sx, x8, nullptr, stream)
                      : launch_cast(X, M, K, FP8_E4M3, sx, x8, nullptr, stream);
   if (e != hipSuccess) return FP8_ERR_HIP;
-  return hip_status(launch_gemm(x8, FP8_E4M3, sx, w8t, FP8_E4M3, sw, M, N, K, Y, stream));
+  return hip_status(launch_gemm(x8, FP8_E4M3, false, sx, w8t, FP8_E4M3, false, sw, M, N, K, Y, stream));
 }
 
-fp8_status fp8_wgrad_fp8(const uint8_t* x8t, const fp8_scale_t* sx, const uint8_t* dy8t,
-                         const fp8_scale_t* sdy, int64_t K, int64_t N, int64_t M, int margin, int mu_log2,
-                         void* dW_bf16, fp8_scale_t* s_dw, uint8_t* dw8, uint8_t* dw8t, hipStream_t stream) {
+fp8_status fp8_wgrad_fp8(const uint8_t* x8, fp8_layout lx, const fp8_scale_t* sx, const uint8_t* dy8,
+                         fp8_layout ldy, const fp8_scale_t* sdy, int64_t K, int64_t N, int64_t M, int margin,
+                         int mu_log2, void* dW_bf16, fp8_scale_t* s_dw, uint8_t* dw8, uint8_t* dw8t,
+                         hipStream_t stream) {
   if (K < 0 || N < 0 || M < 0 || !int_ok(margin) || !int_ok(mu_log2)) return FP8_ERR_INVALID;
+  if ((lx != FP8_OPERAND_ROWS && lx != FP8_OPERAND_COLS) || (ldy != FP8_OPERAND_ROWS && ldy != FP8_OPERAND_COLS))
+    return FP8_ERR_INVALID;
   if (!sx || !aligned16(sx) || !sdy || !aligned16(sdy) || !s_dw || !aligned16(s_dw)) return FP8_ERR_INVALID;
   if (K % 16 || N % 16 || M % 16 || K >= kMaxDim || N >= kMaxDim || M >= kMaxDim || !gemm_fits(K, N, M))
     return FP8_ERR_UNSUPPORTED;
   if (K > 0 && N > 0) {
     if (!dW_bf16 || !aligned16(dW_bf16) || !dw8 || !aligned16(dw8)) return FP8_ERR_INVALID;
     if (dw8t && !aligned16(dw8t)) return FP8_ERR_INVALID;
-    if (M > 0 && (!x8t || !aligned16(x8t) || !dy8t || !aligned16(dy8t))) return FP8_ERR_INVALID;
+    if (M > 0 && (!x8 || !aligned16(x8) || !dy8 || !aligned16(dy8))) return FP8_ERR_INVALID;
   }
   hipError_t e = K > 0 && N > 0
-                     ? launch_gemm_wgrad_amax(x8t, sx, dy8t, sdy, K, N, M, dW_bf16, s_dw, stream)
+                     ? launch_gemm_wgrad_amax(x8, lx == FP8_OPERAND_COLS, sx, dy8, ldy == FP8_OPERAND_COLS, sdy, K,
+                                              N, M, dW_bf16, s_dw, stream)
                      : launch_amax_gen(nullptr, 0, s_dw, stream);  // an empty max, so the record publishes
   if (e != hipSuccess) return FP8_ERR_HIP;
   return hip_status(launch_wgrad_cast(dW_bf16, K, N, s_dw, dw8, dw8t, margin, mu_log2, stream));

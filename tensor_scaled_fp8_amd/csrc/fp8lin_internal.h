@@ -113,10 +113,12 @@ hipError_t launch_amax_gen(const void* x, int64_t n, fp8_scale_t* s, hipStream_t
 // amax pass + cast that derives the scale (fp8_quantize)
 hipError_t launch_quantize(const void* x, int64_t rows, int64_t cols, int fmt, int margin, int mu_log2,
                            fp8_scale_t* s, uint8_t* out_row, uint8_t* out_t, hipStream_t st);
-hipError_t launch_gemm(const uint8_t* A, int fa, const fp8_scale_t* sa, const uint8_t* B, int fb,
+// ta / tb: operand stored reduction-major (A [R, M], B [R, N]) instead of
+// one row per output index (A [M, R], B [N, R])
+hipError_t launch_gemm(const uint8_t* A, int fa, bool ta, const fp8_scale_t* sa, const uint8_t* B, int fb, bool tb,
                        const fp8_scale_t* sb, int64_t M, int64_t N, int64_t R, void* C,
                        hipStream_t st);
-hipError_t launch_gemm_wgrad_amax(const uint8_t* A, const fp8_scale_t* sa, const uint8_t* B,
+hipError_t launch_gemm_wgrad_amax(const uint8_t* A, bool ta, const fp8_scale_t* sa, const uint8_t* B, bool tb,
                                   const fp8_scale_t* sb, int64_t M, int64_t N, int64_t R, void* C,
                                   fp8_scale_t* s_out, hipStream_t st);
 // E5M2 derive-cast of a weight gradient whose amax the wgrad GEMM merged,

@@ -52,6 +52,7 @@ namespace fp8lin {
 namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v2i __attribute__((ext_vector_type(2)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -71,6 +72,7 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef LDS_AS uint8_t lds_u8;
 typedef LDS_AS u32x4 lds_u32x4;
 typedef LDS_AS u32x2 lds_u32x2;
+typedef LDS_AS v2i lds_v2i;
 
 // 16-byte chunk swizzle of a 128-byte LDS row (two rows share one 256-byte
 // bank line). A fragment read has each lane take one chunk of row
@@ -118,7 +120,11 @@ __device__ inline void block_sync_lds() {
 // amax pass of fp8_quantize does; tag = s_out->epoch + 1), so a following
 // derive-cast of C needs no amax pass; block 0 also clears
 // s_out->sat_count for that cast.
-template <int FA, int FB, bool AMAX>
+// TA / TB: operand layout. false: one row per output index with the R
+// reduction bytes contiguous (A [M, R], B [N, R]); true: reduction-major
+// (A [R, M], B [R, N]), staged in LDS as [k][output] and turned into MFMA
+// fragments by transposing LDS reads.
+template <int FA, int FB, bool AMAX, bool TA, bool TB>
 __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ B, const fp8_scale_t* __restrict__ sa,
     const fp8_scale_t* __restrict__ sb, int M, int N, int R, uint16_t* __restrict__ C, int tiles_m,
@@ -152,21 +158,41 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
   const int wm = w >> 1, wn = w & 1;
 
   // ---- loads: wave w fills 1 KB blocks 8w..8w+7 of the A and B parts of a
-  // stage; lane l of block b writes row 8b + l/8, LDS chunk l%8, which holds
-  // global chunk (l%8) ^ swz(row). Operands are below 4 GiB, so per-lane
-  // offsets are 32-bit; the stage's k offset is a scalar.
+  // stage (a part is 32 KB). Row-layout operand: lane l of block b writes
+  // row 8b + l/8 (an output index), LDS chunk l%8, which holds global chunk
+  // (l%8) ^ swz(row) of that row's 128 k-bytes; rows past M / N read the
+  // last valid row. Reduction-major operand: lane l of block b writes k-row
+  // 4b + l/16, LDS chunk l%16 of that row's 256 output bytes, which holds
+  // global chunk (l%16) ^ (krow & 7); chunks past M / N read the last valid
+  // chunk, so the tile only ever holds real operand values. Operands are
+  // below 4 GiB, so per-lane offsets are 32-bit; the stage offset is a
+  // scalar (stage * 128 for rows, stage * 128 * M or N for reduction-major).
+  // op_offset: product part p (laundered below) and added part c of lane's
+  // offset for load i.
+  auto op_offset = [&](auto T_, int i, int o0, int O, uint32_t& p, uint32_t& c) {
+    if constexpr (!decltype(T_)::value) {
+      const int row = 8 * (8 * w + i) + (lane >> 3);
+      p = (uint32_t)min(o0 + row, O - 1) * (uint32_t)R;
+      c = 16 * ((lane & 7) ^ swz(row));
+    } else {
+      const int krow = 4 * (8 * w + i) + (lane >> 4);
+      p = (uint32_t)krow * (uint32_t)O;
+      c = (uint32_t)min(o0 + 16 * ((lane & 15) ^ (krow & 7)), O - 16);
+    }
+  };
+  using TAc = std::integral_constant<bool, TA>;
+  using TBc = std::integral_constant<bool, TB>;
   uint32_t offa[8], offb[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int row = 8 * (8 * w + i) + (lane >> 3);
-    const int kc = 16 * ((lane & 7) ^ swz(row));
     // 32-bit products, passed through an empty asm: fused into a 64-bit
     // multiply-add, each offset would occupy a register pair
-    uint32_t pa = (uint32_t)min(m0 + row, M - 1) * (uint32_t)R;
-    uint32_t pb = (uint32_t)min(n0 + row, N - 1) * (uint32_t)R;
+    uint32_t pa, ca, pb, cb;
+    op_offset(TAc{}, i, m0, M, pa, ca);
+    op_offset(TBc{}, i, n0, N, pb, cb);
     asm volatile("" : "+v"(pa), "+v"(pb));
-    offa[i] = pa + kc;
-    offb[i] = pb + kc;
+    offa[i] = pa + ca;
+    offb[i] = pb + cb;
   }
   const int nk = (R + kBK - 1) / kBK;      // stages
   const int nfull = R / kBK;               // full stages (all but a partial last one)
@@ -180,13 +206,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
       __builtin_amdgcn_make_buffer_rsrc((void*)B, (short)0, (int)((uint32_t)N * (uint32_t)R), kRsrcWord3);
   // the 16 loads (8 of A, 8 of B) of one full stage
   auto issue_full = [&](lds_u8* sl, int stage) {
-    const int koff = stage * kBK;  // wave-uniform
+    // wave-uniform; below 2^32 (operands are below 4 GiB), passed as int
+    const int koffa = (int)((uint32_t)stage * kBK * (TA ? (uint32_t)M : 1u));
+    const int koffb = (int)((uint32_t)stage * kBK * (TB ? (uint32_t)N : 1u));
     lds_u8* sa_ = sl + (8 * w) * 1024;
     lds_u8* sb_ = sl + kOpBytes + (8 * w) * 1024;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (LDS_AS void*)(sa_ + i * 1024), 16, (int)offa[i], koff, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (LDS_AS void*)(sb_ + i * 1024), 16, (int)offb[i], koff, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (LDS_AS void*)(sa_ + i * 1024), 16, (int)offa[i], koffa, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (LDS_AS void*)(sb_ + i * 1024), 16, (int)offb[i], koffb, 0, 0);
     }
   };
   // any stage, including a partial last one (k past R zero-filled)
@@ -198,19 +226,29 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
     const int k0 = stage * kBK;
     lds_u8* sa_ = sl + (8 * w) * 1024;
     lds_u8* sb_ = sl + kOpBytes + (8 * w) * 1024;
+    // first k of lane's 16 bytes (row layout) or lane's k-row (reduction-major)
+    auto lane_k = [&](auto T_, int i) -> int {
+      if constexpr (!decltype(T_)::value) {
+        const int row = 8 * (8 * w + i) + (lane >> 3);
+        return k0 + 16 * ((lane & 7) ^ swz(row));
+      } else {
+        return k0 + 4 * (8 * w + i) + (lane >> 4);
+      }
+    };
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int row = 8 * (8 * w + i) + (lane >> 3);
-      const int kc = 16 * ((lane & 7) ^ swz(row));
       lds_u8* da = sa_ + i * 1024;
       lds_u8* db = sb_ + i * 1024;
-      if (k0 + kc < R) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (LDS_AS void*)da, 16, (int)offa[i], k0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (LDS_AS void*)db, 16, (int)offb[i], k0, 0, 0);
-      } else {
+      if (lane_k(TAc{}, i) < R)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (LDS_AS void*)da, 16, (int)offa[i],
+                                                 (int)((uint32_t)k0 * (TA ? (uint32_t)M : 1u)), 0, 0);
+      else
         *(lds_u32x4*)(da + 16 * lane) = (u32x4){0, 0, 0, 0};
+      if (lane_k(TBc{}, i) < R)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (LDS_AS void*)db, 16, (int)offb[i],
+                                                 (int)((uint32_t)k0 * (TB ? (uint32_t)N : 1u)), 0, 0);
+      else
         *(lds_u32x4*)(db + 16 * lane) = (u32x4){0, 0, 0, 0};
-      }
     }
   };
 
@@ -226,7 +264,28 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
   for (int h = 0; h < 2; ++h)
 #pragma unroll
     for (int j = 0; j < 2; ++j) foff[h][j] = frow * kBK + (((4 * h + 2 * g + j) ^ fsw) << 4);
-  const int a_row0 = 128 * wm * kBK, b_row0 = kOpBytes + 128 * wn * kBK;  // wave-uniform
+  // Reduction-major operand: the part holds 128 k-rows of 256 output bytes.
+  // A transposing LDS read (ds_read_b64_tr_b8) works on groups of 16 lanes:
+  // lanes 2r and 2r+1 give the two 8-byte halves of a 16-byte row r
+  // (r = 0..7), and lane i receives byte i of each of the 8 rows. Lane l's
+  // group G = l / 16 covers outputs 16 (G % 2) .. + 15 of a 32-output block
+  // and k-half G / 2; lane 2r + hh of the group points at k-row
+  // 64 h + 32 (G / 2) + 8 t + r, byte 8 hh of the block's chunk, so read t
+  // (t = 0..3) hands each lane k = 8 t .. 8 t + 7 of its k-half for output
+  // (l & 31): the same 32 bytes the row layout reads. k-rows of one read
+  // differ in (k & 7), so with the load swizzle (chunk ^ (k & 7)) they fall
+  // in distinct banks. toff[f]: lane's offset for output block f; reads t
+  // and steps h add 2048 t + 16384 h.
+  int toff[4];
+  {
+    const int G = lane >> 4, j = lane & 15, r = j >> 1;
+#pragma unroll
+    for (int f4 = 0; f4 < 4; ++f4)
+      toff[f4] = (32 * (G >> 1) + r) * 256 + (((2 * f4 + (G & 1)) ^ r) << 4) + 8 * (j & 1);
+  }
+  // wave-uniform fragment bases of A and B
+  const int a_row0 = TA ? 128 * wm : 128 * wm * kBK;
+  const int b_row0 = kOpBytes + (TB ? 128 * wn : 128 * wn * kBK);
   struct Frags {
     v8i a[4], b[4];
   };
@@ -238,12 +297,30 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
     v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
     return v;
   };
+  auto read_frag_t = [&](const lds_u8* p, int h, int f4) -> v8i {
+    v8i v;
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      const v2i x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(p + toff[f4] + 16384 * h + 2048 * tt));
+      v[2 * tt] = x.x;
+      v[2 * tt + 1] = x.y;
+    }
+    return v;
+  };
   auto read_step = [&](const lds_u8* sl, int h, Frags& f) {
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi) f.a[mi] = read_frag(sl + a_row0 + 32 * mi * kBK, h);
+    for (int mi = 0; mi < 4; ++mi) {
+      if constexpr (TA) f.a[mi] = read_frag_t(sl + a_row0, h, mi);
+      else f.a[mi] = read_frag(sl + a_row0 + 32 * mi * kBK, h);
+    }
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni) f.b[ni] = read_frag(sl + b_row0 + 32 * ni * kBK, h);
+    for (int ni = 0; ni < 4; ++ni) {
+      if constexpr (TB) f.b[ni] = read_frag_t(sl + b_row0, h, ni);
+      else f.b[ni] = read_frag(sl + b_row0 + 32 * ni * kBK, h);
+    }
   };
+  // LDS reads per step, spread evenly over its first 8 MFMAs below
+  constexpr int kReadsPer = ((TA ? 4 : 2) + (TB ? 4 : 2)) / 2;
 
   v16f acc[4][4];
 #pragma unroll
@@ -300,8 +377,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
     mfma_all(fr[0]);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, kReadsPer, 0);  // DS read
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -316,9 +393,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
     // outran the load path and stalled issue (measured 2-3 % slower)
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // buffer load to LDS
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, kReadsPer, 0);  // DS read
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);          // buffer load to LDS
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -447,32 +524,44 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
   else drain_all(std::false_type{});
 }
 
-template <int FA, int FB, bool AMAX = false>
+template <int FA, int FB, bool AMAX, bool TA, bool TB>
 hipError_t launch_typed(const uint8_t* A, const fp8_scale_t* sa, const uint8_t* B, const fp8_scale_t* sb,
-                        int64_t M, int64_t N, int64_t R, void* C, hipStream_t st, fp8_scale_t* s_out = nullptr) {
+                        int64_t M, int64_t N, int64_t R, void* C, hipStream_t st, fp8_scale_t* s_out) {
   const int tiles_m = (int)((M + kBM - 1) / kBM), tiles_n = (int)((N + kBN - 1) / kBN);
-  hipLaunchKernelGGL((gemm_nt_kernel<FA, FB, AMAX>), dim3(tiles_m * tiles_n), dim3(kThreads), 0, st, A, B,
-                     sa, sb, (int)M, (int)N, (int)R, (uint16_t*)C, tiles_m, tiles_n, s_out);
+  hipLaunchKernelGGL((gemm_nt_kernel<FA, FB, AMAX, TA, TB>), dim3(tiles_m * tiles_n), dim3(kThreads), 0, st, A,
+                     B, sa, sb, (int)M, (int)N, (int)R, (uint16_t*)C, tiles_m, tiles_n, s_out);
   return hipGetLastError();
+}
+
+template <int FA, int FB>
+hipError_t launch_layouts(const uint8_t* A, bool ta, const fp8_scale_t* sa, const uint8_t* B, bool tb,
+                          const fp8_scale_t* sb, int64_t M, int64_t N, int64_t R, void* C, hipStream_t st) {
+  if (!ta && !tb) return launch_typed<FA, FB, false, false, false>(A, sa, B, sb, M, N, R, C, st, nullptr);
+  if (!ta && tb) return launch_typed<FA, FB, false, false, true>(A, sa, B, sb, M, N, R, C, st, nullptr);
+  if (ta && !tb) return launch_typed<FA, FB, false, true, false>(A, sa, B, sb, M, N, R, C, st, nullptr);
+  return launch_typed<FA, FB, false, true, true>(A, sa, B, sb, M, N, R, C, st, nullptr);
 }
 
 }  // namespace
 
-hipError_t launch_gemm(const uint8_t* A, int fa, const fp8_scale_t* sa, const uint8_t* B, int fb,
-                       const fp8_scale_t* sb, int64_t M, int64_t N, int64_t R, void* C,
-                       hipStream_t st) {
+hipError_t launch_gemm(const uint8_t* A, int fa, bool ta, const fp8_scale_t* sa, const uint8_t* B, int fb,
+                       bool tb, const fp8_scale_t* sb, int64_t M, int64_t N, int64_t R, void* C, hipStream_t st) {
   if (M == 0 || N == 0) return hipSuccess;
-  if (fa == FP8_E4M3 && fb == FP8_E4M3) return launch_typed<0, 0>(A, sa, B, sb, M, N, R, C, st);
-  if (fa == FP8_E5M2 && fb == FP8_E4M3) return launch_typed<1, 0>(A, sa, B, sb, M, N, R, C, st);
-  if (fa == FP8_E4M3 && fb == FP8_E5M2) return launch_typed<0, 1>(A, sa, B, sb, M, N, R, C, st);
-  return launch_typed<1, 1>(A, sa, B, sb, M, N, R, C, st);
+  if (fa == FP8_E4M3 && fb == FP8_E4M3) return launch_layouts<0, 0>(A, ta, sa, B, tb, sb, M, N, R, C, st);
+  if (fa == FP8_E5M2 && fb == FP8_E4M3) return launch_layouts<1, 0>(A, ta, sa, B, tb, sb, M, N, R, C, st);
+  if (fa == FP8_E4M3 && fb == FP8_E5M2) return launch_layouts<0, 1>(A, ta, sa, B, tb, sb, M, N, R, C, st);
+  return launch_layouts<1, 1>(A, ta, sa, B, tb, sb, M, N, R, C, st);
 }
 
-hipError_t launch_gemm_wgrad_amax(const uint8_t* A, const fp8_scale_t* sa, const uint8_t* B,
+hipError_t launch_gemm_wgrad_amax(const uint8_t* A, bool ta, const fp8_scale_t* sa, const uint8_t* B, bool tb,
                                   const fp8_scale_t* sb, int64_t M, int64_t N, int64_t R, void* C,
                                   fp8_scale_t* s_out, hipStream_t st) {
   if (M == 0 || N == 0) return hipSuccess;
-  return launch_typed<FP8_E4M3, FP8_E5M2, true>(A, sa, B, sb, M, N, R, C, st, s_out);
+  constexpr int E4 = FP8_E4M3, E5 = FP8_E5M2;
+  if (!ta && !tb) return launch_typed<E4, E5, true, false, false>(A, sa, B, sb, M, N, R, C, st, s_out);
+  if (!ta && tb) return launch_typed<E4, E5, true, false, true>(A, sa, B, sb, M, N, R, C, st, s_out);
+  if (ta && !tb) return launch_typed<E4, E5, true, true, false>(A, sa, B, sb, M, N, R, C, st, s_out);
+  return launch_typed<E4, E5, true, true, true>(A, sa, B, sb, M, N, R, C, st, s_out);
 }
 
 }  // namespace fp8lin

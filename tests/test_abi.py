@@ -31,7 +31,7 @@ def test_header_functions_all_exported():
     for n in names:
         assert hasattr(lib, n), n
         assert n in _lib.SIGNATURES, f"binding lacks {n}"
-    assert lib.fp8_abi_version() == 5
+    assert lib.fp8_abi_version() == 6
 
 
 def test_status_strings():
@@ -96,12 +96,22 @@ def test_argument_validation_without_launch():
     assert g(_vp(ok), 0, None, _vp(ok), 0, _vp(ok), 16, 16, 16, _vp(ok), None) == INV
     assert g(_vp(ok), 0, _vp(ok), _vp(ok), 0, _vp(ok), -16, 16, 16, _vp(ok), None) == INV
     assert g(_vp(ok), 0, _vp(ok), None, 0, _vp(ok), 16, 16, 16, _vp(ok), None) == INV
+    gl = lib.fp8_gemm
+    assert gl(_vp(ok), 0, 2, _vp(ok), _vp(ok), 0, 0, _vp(ok), 16, 16, 16, _vp(ok), None) == INV
+    assert gl(_vp(ok), 0, 0, _vp(ok), _vp(ok), 0, -1, _vp(ok), 16, 16, 16, _vp(ok), None) == INV
+    assert gl(_vp(ok), 0, 1, _vp(ok), _vp(ok), 0, 1, _vp(ok), 16, 16, 40, _vp(ok), None) == UNS
+    assert gl(_vp(ok), 0, 1, _vp(ok), None, 0, 1, _vp(ok), 16, 16, 16, _vp(ok), None) == INV
     # linear: workspace checks
     ws = _lib.LinearWs(ok, ok, ok, ok, ok, ok, ok, ok, ok)
     assert lib.fp8_linear_fwd(_vp(ok), _vp(ok), 16, 16, 16, 0, None, _vp(ok), None) == INV
     assert lib.fp8_linear_fwd(_vp(ok), _vp(ok), 16, 24, 16, 0, ctypes.byref(ws), _vp(ok), None) == UNS
     ws_bad = _lib.LinearWs(ok, ok, ok, ok, None, ok, ok, ok, ok)
     assert lib.fp8_linear_bwd(_vp(ok), 16, 16, 16, 0, 0, ctypes.byref(ws_bad), None, None, None) == INV
+    # the transposed copies are optional, but aligned when given
+    ws_mis = _lib.LinearWs(ok, ok + 4, ok, None, ok, None, ok, ok, ok)
+    assert lib.fp8_linear_fwd(_vp(ok), _vp(ok), 16, 16, 16, 0, ctypes.byref(ws_mis), _vp(ok), None) == INV
+    ws_nox = _lib.LinearWs(None, None, ok, None, ok, None, ok, ok, ok)
+    assert lib.fp8_linear_fwd(_vp(ok), _vp(ok), 16, 16, 16, 0, ctypes.byref(ws_nox), _vp(ok), None) == INV
     # fixed bias: only [-126, 126]
     assert lib.fp8_scale_fixed(_vp(ok), 127, None) == INV
     assert lib.fp8_scale_fixed(_vp(ok), -127, None) == INV
@@ -123,7 +133,8 @@ def test_argument_validation_without_launch():
     # FP8 weight gradient
     wg = lib.fp8_wgrad_fp8
     wargs = lambda **kw: [kw.get(k, d) for k, d in (
-        ("x8t", _vp(ok)), ("sx", _vp(ok)), ("dy8t", _vp(ok)), ("sdy", _vp(ok)), ("K", 16), ("N", 16),
+        ("x8", _vp(ok)), ("lx", 0), ("sx", _vp(ok)), ("dy8", _vp(ok)), ("ldy", 1), ("sdy", _vp(ok)), ("K", 16),
+        ("N", 16),
         ("M", 16), ("margin", 0), ("mu", 0), ("dW", _vp(ok)), ("s_dw", _vp(ok)), ("dw8", _vp(ok)),
         ("dw8t", None), ("st", None))]
     assert wg(*wargs(M=24)) == UNS
@@ -133,7 +144,9 @@ def test_argument_validation_without_launch():
     assert wg(*wargs(dW=_vp(ok + 2))) == INV
     assert wg(*wargs(dw8t=_vp(ok + 1))) == INV
     assert wg(*wargs(mu=3000)) == INV
-    assert wg(*wargs(x8t=None)) == INV
+    assert wg(*wargs(x8=None)) == INV
+    assert wg(*wargs(lx=2)) == INV
+    assert wg(*wargs(ldy=-1)) == INV
     # O2 Adam
     ad = lib.fp8_adam_step
     aargs = lambda **kw: [kw.get(k, d) for k, d in (

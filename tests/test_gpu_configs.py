@@ -97,7 +97,7 @@ def test_full_size_linear(wl_idx, li):
     wl = WORKLOADS[wl_idx]
     L = wl.linears[li]
     X, W, dY = linear_inputs(wl, li)
-    ws = tsf.LinearWorkspace(L.M, L.K, L.N)
+    ws = tsf.LinearWorkspace(L.M, L.K, L.N, transposed=True)
     Xd, Wd, dYd = to_dev_bf16(X), to_dev_bf16(W), to_dev_bf16(dY)
     Y = tsf.fp8_linear_fwd(Xd, Wd, ws, wl.margin)
     dX, dW = tsf.fp8_linear_bwd(dYd, ws, wl.margin, wl.mu_log2)

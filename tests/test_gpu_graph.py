@@ -46,14 +46,14 @@ class Step:
     def run(self):
         tsf.fp8_linear_fwd(self.X, self.W, self.ws, Y=self.Y)
         tsf.fp8_linear_bwd(self.dY, self.ws, mu_log2=1, dX=self.dX, dW=self.dW)
-        tsf.fp8_wgrad_fp8(self.ws.x8t, self.ws.sx, self.ws.dy8t, self.ws.sdy, 0, 2, dW=self.dW2, s_dw=self.s_dw,
-                          dw8=self.dw8, dw8t=self.dw8t, transposed=True)
+        tsf.fp8_wgrad_fp8(self.ws.x8, self.ws.sx, self.ws.dy8, self.ws.sdy, 0, 2, dW=self.dW2, s_dw=self.s_dw,
+                          dw8=self.dw8, dw8t=self.dw8t, transposed=True, x_layout="cols", dy_layout="cols")
         tsf.fp8_amax_scale(self.dY, "e5m2", self.s_a, 0, 1)
 
     def outputs(self):
         ws = self.ws
         return {"Y": self.Y, "dX": self.dX, "dW": self.dW, "dW2": self.dW2, "dw8": self.dw8, "dw8t": self.dw8t,
-                "x8": ws.x8, "x8t": ws.x8t, "w8": ws.w8, "w8t": ws.w8t, "dy8": ws.dy8, "dy8t": ws.dy8t}
+                "x8": ws.x8, "w8": ws.w8, "dy8": ws.dy8}
 
     def records(self):
         recs = {"sx": self.ws.sx, "sw": self.ws.sw, "sdy": self.ws.sdy, "s_dw": self.s_dw, "s_a": self.s_a}

@@ -241,10 +241,10 @@ def test_gemm_extremes_saturated_operands():
 @pytest.mark.parametrize("shift", [-252, -140, -95, -94, -60, 0, 40, 72, 73, 100])
 @pytest.mark.parametrize("fa,fb", [(0, 0), (1, 0), (0, 1), (1, 1)])
 def test_gemm_dequant_scale_range(shift, fa, fb):
-    """2^-(ba+bb) across the whole bias range, on both sides of the range the
-    kernel folds into the MFMA operand scales ([-94, 72]): outputs that
-    underflow to zero, land on bf16 subnormals, or sit near the top of the
-    bf16 range all follow the oracle's single rounding."""
+    """2^-(ba+bb) across the whole bias range (around [-94, 72], where the
+    scaling could also be folded into the MFMA operand scales exactly):
+    outputs that underflow to zero, land on bf16 subnormals, or sit near the
+    top of the bf16 range all follow the oracle's single rounding."""
     g = np.random.Generator(np.random.PCG64(1000 + shift + 4 * fa + fb))
     ba = -shift // 2
     bb = -shift - ba
@@ -271,11 +271,15 @@ def test_gemm_degenerate():
 # ---------------------------------------------------------------- composed linear
 @pytest.mark.parametrize("M,K,N,margin,mu", [(512, 768, 3072, 0, 0), (272, 400, 528, 1, -1),
                                              (64, 128, 48, 0, 3)])
-def test_linear_fwd_bwd_vs_oracle(M, K, N, margin, mu):
+@pytest.mark.parametrize("transposed", [False, True])
+def test_linear_fwd_bwd_vs_oracle(M, K, N, margin, mu, transposed):
+    """The GEMMs read the row-major FP8 copies (reduction-major where
+    needed); the transposed copies are written only when the workspace
+    has them, and then match the oracle too."""
     X = draw_normal_bf16(1, (M, K), 1.0)
     W = draw_normal_bf16(2, (K, N), 0.02)
     dY = draw_normal_bf16(3, (M, N), 1e-4)
-    ws = tsf.LinearWorkspace(M, K, N)
+    ws = tsf.LinearWorkspace(M, K, N, transposed=transposed)
     Y = tsf.fp8_linear_fwd(to_dev_bf16(X), to_dev_bf16(W), ws, margin)
     dX, dW = tsf.fp8_linear_bwd(to_dev_bf16(dY), ws, margin, mu)
     ref = oracle.linear_fwd_bwd(X, W, dY, margin, mu)
@@ -283,7 +287,7 @@ def test_linear_fwd_bwd_vs_oracle(M, K, N, margin, mu):
         r = tsf.read_scale(s)
         assert f32_bits(r["amax"]) == f32_bits(ref[key]["amax"])
         assert (r["bias"], r["flags"]) == (ref[key]["bias"], ref[key]["flags"]), key
-    for key in ("x8", "x8t", "w8", "w8t", "dy8", "dy8t"):
+    for key in ("x8", "x8t", "w8", "w8t", "dy8", "dy8t") if transposed else ("x8", "w8", "dy8"):
         assert np.array_equal(u8(getattr(ws, key)), ref[key]), key
     for key, t in (("Y", Y), ("dX", dX), ("dW", dW)):
         bits, c64, tol = ref[key]

@@ -1,0 +1,91 @@
+"""fp8_gemm with reduction-major operands (FP8_OPERAND_COLS), through the C ABI.
+
+[Perez et al. review, "Proposed method", bullet 3: the matmul runs on the
+scaled FP8 operands.] A reduction-major operand is the row-major FP8 copy
+of a tensor read transposed (A [R, M], B [R, N]), so the forward and the
+weight-gradient GEMMs need no transposed FP8 copies. The kernel feeds the
+MFMA the same 32 k-bytes per lane in either layout, so every layout must
+give the row-layout result bit for bit; the row-layout result is checked
+against the float64 oracle within the GEMM tolerance. Shapes cover partial
+tiles in M and N (chunks past the edge read the last valid chunk), partial
+last stages in R (zero-filled k-rows), the smallest sizes and every format
+pair."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import E4M3, E5M2
+import tensor_scaled_fp8_amd as tsf
+from tests.gpu_util import bf16_bits, scale_record, to_dev_u8
+
+pytestmark = pytest.mark.gpu
+FMT = {0: E4M3, 1: E5M2}
+NAME = {0: "e4m3", 1: "e5m2"}
+LAYOUTS = [("rows", "cols"), ("cols", "rows"), ("cols", "cols")]
+
+
+def _operands(M, N, R, fa, fb, seed):
+    g = np.random.Generator(np.random.PCG64(seed))
+    A = oracle.encode(g.standard_normal((M, R)) * 40, FMT[fa])
+    B = oracle.encode(g.standard_normal((N, R)) * 40, FMT[fb])
+    return A, B
+
+
+def _run(A, fa, ba, B, fb, bb, la, lb):
+    a = to_dev_u8(np.ascontiguousarray(A.T) if la == "cols" else A)
+    b = to_dev_u8(np.ascontiguousarray(B.T) if lb == "cols" else B)
+    return tsf.fp8_gemm(a, NAME[fa], scale_record(ba), b, NAME[fb], scale_record(bb), a_layout=la, b_layout=lb)
+
+
+@pytest.mark.parametrize("M,N,R", [(272, 528, 400), (256, 256, 128), (16, 16, 16), (784, 272, 2064),
+                                   (16, 1040, 528), (512, 768, 144), (48, 32, 1040)])
+@pytest.mark.parametrize("fa,fb", [(0, 0), (1, 0), (0, 1), (1, 1)])
+def test_layouts_bit_identical_and_oracle(M, N, R, fa, fb):
+    A, B = _operands(M, N, R, fa, fb, M + 3 * N + 7 * R + 11 * fa + 13 * fb)
+    ref = _run(A, fa, 6, B, fb, 11, "rows", "rows")
+    torch.cuda.synchronize()
+    bits, _, tol = oracle.gemm_nt(A, FMT[fa], 6, B, FMT[fb], 11)
+    err = np.abs(oracle.bf16_to_f64(bf16_bits(ref)) - oracle.bf16_to_f64(bits))
+    assert not np.any(~(err <= tol)), float(np.max(err / tol))
+    for la, lb in LAYOUTS:
+        out = _run(A, fa, 6, B, fb, 11, la, lb)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), (la, lb)
+
+
+def test_layouts_one_hot_exact():
+    """B = permutation of 1.0 codes, read reduction-major: C reproduces
+    columns of A exactly (pins the k pairing of the transposing reads)."""
+    g = np.random.Generator(np.random.PCG64(78))
+    codes = np.array([c for c in range(256) if np.isfinite(oracle.decode_table(E4M3)[c])], np.uint8)
+    for M, R in ((32, 64), (288, 320), (16, 16)):
+        A = g.choice(codes, size=(M, R))
+        one = int(oracle.encode(np.array([1.0]), E4M3)[0])
+        perm = g.permutation(R)
+        B = np.zeros((R, R), np.uint8)
+        B[np.arange(R), perm] = one
+        want, _, _ = oracle.gemm_nt(A, E4M3, 2, B, E4M3, -1)
+        for la, lb in LAYOUTS:
+            out = _run(A, 0, 2, B, 0, -1, la, lb)
+            torch.cuda.synchronize()
+            assert np.array_equal(bf16_bits(out), want), (M, R, la, lb)
+
+
+def test_layouts_full_size_gpt7b_shapes():
+    """The step's reduction-major GEMMs at full size: forward of up
+    (4096 x 16384 x 4096, B = w8 reduction-major) and the weight gradient
+    of down (16384 x 4096 x 4096, both operands reduction-major) equal the
+    row-layout GEMM on the transposed copies bit for bit."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5)
+    s_a, s_b = scale_record(6), scale_record(11)
+    for (M, N, R), (la, lb) in (((4096, 16384, 4096), ("rows", "cols")), ((16384, 4096, 4096), ("cols", "cols"))):
+        a_rows = torch.randint(0, 0x78, (M, R), dtype=torch.uint8, device="cuda", generator=g)
+        b_rows = torch.randint(0, 0x78, (N, R), dtype=torch.uint8, device="cuda", generator=g)
+        a = a_rows.t().contiguous() if la == "cols" else a_rows
+        b = b_rows.t().contiguous() if lb == "cols" else b_rows
+        ref = tsf.fp8_gemm_nt(a_rows, "e4m3", s_a, b_rows, "e5m2", s_b)
+        out = tsf.fp8_gemm(a, "e4m3", s_a, b, "e5m2", s_b, a_layout=la, b_layout=lb)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), (M, N, R, la, lb)

@@ -87,7 +87,7 @@ def test_cached_forward_equals_linear_fwd_and_oracle(M, K, N):
     xb = oracle.f64_to_bf16_rne(g.standard_normal((M, K)))
     wb = oracle.f64_to_bf16_rne(g.standard_normal((K, N)) * 0.02)
     X, W = to_dev_bf16(xb), to_dev_bf16(wb)
-    ws = tsf.LinearWorkspace(M, K, N)
+    ws = tsf.LinearWorkspace(M, K, N, transposed=True)
     Y_train = tsf.fp8_linear_fwd(X, W, ws)
     w8t, sw = tsf.prepare_weight(W)
     x8 = torch.empty((M, K), dtype=torch.uint8, device="cuda")

@@ -132,10 +132,30 @@ def test_record_reuse_with_shrinking_gradients():
         _check_chain(dW, dw8, None, s_dw, 0, 0)
 
 
+@pytest.mark.parametrize("M,K,N,margin,mu", [(400, 272, 528, 0, 0), (784, 2064, 272, 0, -1), (16, 16, 16, 0, 0),
+                                             (128, 528, 1040, 2, 3)])
+def test_wgrad_fp8_row_major_operands(M, K, N, margin, mu):
+    """The row-major FP8 copies X [M,K] and dY [M,N], read reduction-major,
+    give the transposed-copy result byte for byte (dW, E5M2 codes, record)."""
+    xb, dyb = _operands(M, K, N, M + 5 * K + 3 * N)
+    x8t, sx, dy8t, sdy = _fp8_operands(xb, dyb, margin, mu)
+    x8, _ = tsf.fp8_quantize(to_dev_bf16(xb), "e4m3", tsf.new_scale(1)[0], margin, 0, transposed=False)
+    dy8, _ = tsf.fp8_quantize(to_dev_bf16(dyb), "e5m2", tsf.new_scale(1)[0], margin, mu, transposed=False)
+    a = tsf.fp8_wgrad_fp8(x8t, sx, dy8t, sdy, margin, mu, transposed=True)
+    b = tsf.fp8_wgrad_fp8(x8, sx, dy8, sdy, margin, mu, transposed=True, x_layout="cols", dy_layout="cols")
+    torch.cuda.synchronize()
+    assert torch.equal(a[0].view(torch.int16), b[0].view(torch.int16))
+    assert torch.equal(a[1], b[1]) and torch.equal(a[2], b[2])
+    ra, rb = tsf.read_scale(a[3]), tsf.read_scale(b[3])
+    assert all(ra[k] == rb[k] for k in ("bias", "flags", "scale", "sat_count")) and \
+        f32_bits(ra["amax"]) == f32_bits(rb["amax"])
+    _check_chain(b[0], b[1], b[2], b[3], margin, mu)
+
+
 def test_wgrad_fp8_full_size_gpt7b_up():
-    """Full size (dW 4096 x 16384 from 4096 tokens): record and every E5M2
-    byte bit-exact vs the oracle on the kernel's dW, and identical to the
-    unfused sequence."""
+    """Full size (dW 4096 x 16384 from 4096 tokens), from the training
+    step's row-major FP8 copies: record and every E5M2 byte bit-exact vs the
+    oracle on the kernel's dW, and identical to the unfused sequence."""
     wl = WORKLOADS[2]
     li = [l.name for l in wl.linears].index("up")
     L = wl.linears[li]
@@ -143,8 +163,9 @@ def test_wgrad_fp8_full_size_gpt7b_up():
     ws = tsf.LinearWorkspace(L.M, L.K, L.N)
     tsf.fp8_linear_fwd(to_dev_bf16(X), to_dev_bf16(W), ws)
     tsf.fp8_linear_bwd(to_dev_bf16(dY), ws, need_dx=False, need_dw=False)
-    dW, dw8, _, s_dw = tsf.fp8_wgrad_fp8(ws.x8t, ws.sx, ws.dy8t, ws.sdy, wl.margin, 0)
-    dW2 = tsf.fp8_gemm_nt(ws.x8t, "e4m3", ws.sx, ws.dy8t, "e5m2", ws.sdy)
+    dW, dw8, _, s_dw = tsf.fp8_wgrad_fp8(ws.x8, ws.sx, ws.dy8, ws.sdy, wl.margin, 0, x_layout="cols",
+                                         dy_layout="cols")
+    dW2 = tsf.fp8_gemm(ws.x8, "e4m3", ws.sx, ws.dy8, "e5m2", ws.sdy, a_layout="cols", b_layout="cols")
     s2 = tsf.new_scale(1)[0]
     q2, _ = tsf.fp8_quantize(dW2, "e5m2", s2, transposed=False)
     torch.cuda.synchronize()

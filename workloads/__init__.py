@@ -51,10 +51,12 @@ class Workload:
     def flops_fwd_bwd(self) -> int:
         return sum(6 * l.M * l.K * l.N for l in self.linears)
 
-    def quant_bytes(self) -> int:
-        """HBM bytes of amax (2 B/elem read) + cast-transpose (2 B read,
-        2 B written) over X, W and dY of every linear: 6 B per element."""
-        return sum(6 * (l.M * l.K + l.K * l.N + l.M * l.N) for l in self.linears)
+    def quant_bytes(self, transposed: bool = False) -> int:
+        """HBM bytes of amax (2 B/elem read) + cast (2 B read, 1 B written per
+        FP8 copy) over X, W and dY of every linear: 5 B per element for the
+        row-major copy alone, 6 B with the transposed copy as well."""
+        per = 6 if transposed else 5
+        return sum(per * (l.M * l.K + l.K * l.N + l.M * l.N) for l in self.linears)
 
 
 def _layer(index, name, M, d, qkv_out, mlp, sigma_w, sigma_dy, margin=0):
