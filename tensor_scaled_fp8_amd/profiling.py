@@ -53,14 +53,16 @@ def kernel_stats(d: str) -> dict:
 
 
 def _short(name: str) -> str:
-    for key in ("gemm_nt_kernel<0, 0>", "gemm_nt_kernel<1, 0>", "gemm_nt_kernel<0, 1>", "gemm_nt_kernel<1, 1>"):
+    """Kernel name without namespaces and parameter list; template arguments
+    kept (they select formats, layouts and variants)."""
+    for key in ("gemm_nt_kernel<", "cast_kernel<"):
         if key in name:
-            return key
-    for key in ("amax_finish_kernel", "amax_kernel", "cast_kernel<0>", "cast_kernel<1>", "scale_kernel",
-                "copyBuffer"):
-        if key in name:
-            return key
-    return name[:60]
+            return name[name.index(key):].split(">")[0] + ">"
+    base = name.replace("(anonymous namespace)::", "")
+    if base.startswith("void "):
+        base = base[5:]
+    base = base.split("(")[0].split("<")[0]
+    return base.split("::")[-1][:60]
 
 
 def stats_markdown(d: str, title: str, command: str) -> str:
