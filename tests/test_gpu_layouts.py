@@ -89,3 +89,27 @@ def test_layouts_full_size_gpt7b_shapes():
         out = tsf.fp8_gemm(a, "e4m3", s_a, b, "e5m2", s_b, a_layout=la, b_layout=lb)
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), (M, N, R, la, lb)
+
+
+def test_layouts_operand_of_2gib():
+    """A 2 GiB B operand (N x R = 2^31 bytes, the top bit of the 32-bit
+    offsets in use) in both layouts: the results are identical, and sampled
+    output columns equal the oracle's within tolerance."""
+    M, N, R = 256, 65536, 32768
+    g = torch.Generator(device="cuda")
+    g.manual_seed(11)
+    a = torch.randint(0, 0x78, (M, R), dtype=torch.uint8, device="cuda", generator=g)
+    b_rows = torch.randint(0, 0x78, (N, R), dtype=torch.uint8, device="cuda", generator=g)
+    s_a, s_b = scale_record(3), scale_record(4)
+    ref = tsf.fp8_gemm(a, "e4m3", s_a, b_rows, "e4m3", s_b)
+    cols = torch.from_numpy(np.random.Generator(np.random.PCG64(12)).choice(N, size=6, replace=False)).cuda()
+    cols = torch.cat([cols, torch.tensor([0, N - 1], device="cuda")])
+    b_sample = b_rows[cols].cpu().numpy()
+    b_t = b_rows.t().contiguous()
+    del b_rows
+    out = tsf.fp8_gemm(a, "e4m3", s_a, b_t, "e4m3", s_b, b_layout="cols")
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+    bits, _, tol = oracle.gemm_nt(a.cpu().numpy(), E4M3, 3, b_sample, E4M3, 4)
+    got = oracle.bf16_to_f64(bf16_bits(out[:, cols]))
+    assert np.all(np.abs(got - oracle.bf16_to_f64(bits)) <= tol)
