@@ -194,6 +194,24 @@ def main():
             p[1] += 1
     kernels["gemm_by_launch"] = {lb: {"us": round(t * 1e3 / n, 1), "TFLOP/s": round(fl / (t / n * 1e-3) / 1e12, 1)}
                                  for lb, (t, n, fl) in per.items()}
+    # per tensor (warm, inside the step) and per linear (6*M*K*N over its three GEMMs)
+    qt = {}
+    for kind, label, nbytes, _, t in brk:
+        if kind == "quant":
+            q = qt.setdefault(label, [0.0, 0, nbytes])
+            q[0] += t
+            q[1] += 1
+    kernels["amax+cast_by_tensor"] = {lb: {"us": round(t * 1e3 / n, 1), "GB/s": round(b / (t / n * 1e-3) / 1e9, 1)}
+                                      for lb, (t, n, b) in qt.items()}
+    lt = {}
+    for kind, label, _, fl, t in timed:
+        if kind == "gemm":
+            e = lt.setdefault(label.split(".")[0], [0.0, 0.0])
+            e[0] += t
+            e[1] += fl
+    kernels["gemm_by_linear"] = {n: {"us_per_step": round(t * 1e3 / args.steps, 1),
+                                     "TFLOP/s": round(f / (t * 1e-3) / 1e12, 1)} for n, (t, f) in lt.items()}
+    kernels["amax+cast_cold"] = quantize_cold(tsf, torch, lin, margin, mu, hip)
     kernels["note"] = ("gemm: events in the timed region; amax+cast (fp8_quantize: amax pass + "
                        f"cast kernel): a separate pass of {args.breakdown_steps} steps with events "
                        "around every call")
@@ -227,6 +245,32 @@ def main():
     if check is not None:
         out["check"] = check
     print(json.dumps(out), flush=True)
+
+
+def quantize_cold(tsf, torch, lin, margin, mu, hip, reps=3):
+    """fp8_quantize of every tensor of the step with the caches cold: a
+    512 MB fill runs before each timed call (the 256 MB MALL would otherwise
+    hold part of the tensor). Median of reps; 5 B per element."""
+    import statistics
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=lin[0]["X"].device)
+    out = {}
+    for d in lin:
+        ws, n = d["ws"], d["L"].name
+        for label, x, fmt, s, q, m in ((f"{n}.X", d["X"], "e4m3", ws.sx, ws.x8, 0),
+                                       (f"{n}.W", d["W"], "e4m3", ws.sw, ws.w8, 0),
+                                       (f"{n}.dY", d["dY"], "e5m2", ws.sdy, ws.dy8, mu)):
+            ts = []
+            for r in range(reps):
+                scratch.fill_(r)
+                e0 = hip.record()
+                tsf.fp8_quantize(x, fmt, s, margin, m, q, transposed=False)
+                e1 = hip.record()
+                torch.cuda.synchronize()
+                ts.append(hip.elapsed_ms(e0, e1))
+            t = statistics.median(ts)
+            out[label] = {"us": round(t * 1e3, 1), "GB/s": round(5 * x.numel() / (t * 1e-3) / 1e9, 1)}
+    del scratch
+    return out
 
 
 def inference_pass(tsf, torch, lin, margin, steps, warmup):

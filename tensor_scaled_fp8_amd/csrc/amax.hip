@@ -31,7 +31,10 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr int kUnroll = 8;        // 16-byte loads in flight per thread
-constexpr int kMaxBlocks = 512;   // 2 blocks per CU on 256 CUs (one merge atomic each at most)
+// 1.5 blocks per CU on 256 CUs (one merge atomic each at most): the best of
+// 256 / 384 / 512 / 1024 / 2048 on 32-128 MB tensors; more blocks end with
+// more merges on the one word and measured slower
+constexpr int kMaxBlocks = 384;
 
 __device__ inline u16x2 as_u16x2(uint32_t v) { return __builtin_bit_cast(u16x2, v); }
 
