@@ -431,17 +431,14 @@ class HipEvents:
 
 def gemm_traffic(path):
     """Measured HBM bytes per GEMM launch from a committed counter summary,
-    reported only while the GEMM source is the one the counters were taken
-    on (sha256 of gemm.hip recorded in the summary)."""
-    import hashlib
+    reported only while the GEMM code is the one the counters were taken on
+    (sha256 of gemm.hip without comments, recorded in the summary)."""
+    from tensor_scaled_fp8_amd.profiling import gemm_code_sha256
     if not path or not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    src = os.path.join(ROOT, "tensor_scaled_fp8_amd", "csrc", "gemm.hip")
-    with open(src, "rb") as f:
-        sha = hashlib.sha256(f.read()).hexdigest()
-    if rec.get("gemm_source_sha256") != sha:
+    if rec.get("gemm_code_sha256") != gemm_code_sha256():
         return None
     return round(rec["gemm_bytes_per_launch"])
 

@@ -1,6 +1,10 @@
-// a4-a6 FP8 GEMM, NT form, on CDNA4 FP8/BF8 MFMA with FP32 accumulation and
-// a dequantising bf16 epilogue:
-//   C[i, j] = bf16_rne( 2^-(bias_a + bias_b) * sum_r A[i, r] * B[j, r] )
+// a4-a6 FP8 GEMM on CDNA4 FP8/BF8 MFMA with FP32 accumulation and a
+// dequantising bf16 epilogue:
+//   C[i, j] = bf16_rne( 2^-(bias_a + bias_b) * sum_r A(i, r) * B(j, r) )
+// with each operand stored either with one row per output index and the
+// reduction contiguous (A [M, R], B [N, R]) or reduction-major (A [R, M],
+// B [R, N]: a row-major FP8 copy read transposed), so the forward, dgrad
+// and wgrad GEMMs all read the same row-major copies of X, W and dY.
 // [Perez et al. review, "Proposed method", bullet 3: the matmul runs on the
 // scaled FP8 operands and the scaling is undone after it; bullet 4: E4 for
 // weights/activations, E5 for gradients, so the backward GEMMs mix formats].
@@ -41,6 +45,9 @@
 //  * Tiles are numbered so that each XCD (workgroups are dealt round-robin
 //    over the 8 XCDs) works on one contiguous, row-grouped region of C and
 //    its operand panels stay in that XCD's L2.
+//  * Reduction-major operands are staged as [k][output] and turned into
+//    the same fragments by transposing LDS reads (ds_read_b64_tr_b8), so
+//    the MFMAs see identical operands in either layout.
 //  * Rows past M or N read a clamped (valid) row and are never stored; k
 //    past R is zero-filled in LDS, so any M, N, R that are multiples of 16
 //    work.

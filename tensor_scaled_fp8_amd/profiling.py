@@ -106,11 +106,19 @@ def traffic(fetch_dir: str, write_dir: str, kernel: str, copy_bytes: int) -> dic
     out["gemm_bytes_per_launch"] = out["fetch_bytes_per_dispatch"] + out["write_bytes_per_dispatch"]
     out["kernel"] = kernel
     out["copy_bytes"] = copy_bytes
-    import hashlib
-    src = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc", "gemm.hip")
-    with open(src, "rb") as f:
-        out["gemm_source_sha256"] = hashlib.sha256(f.read()).hexdigest()
+    out["gemm_code_sha256"] = gemm_code_sha256()
     return out
+
+
+def gemm_code_sha256() -> str:
+    """sha256 of csrc/gemm.hip with // comments and blank lines removed, so
+    the stamp changes with the code and not with its comments."""
+    import hashlib
+    import re
+    src = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc", "gemm.hip")
+    with open(src) as f:
+        lines = [re.sub(r"//.*$", "", ln).rstrip() for ln in f]
+    return hashlib.sha256("\n".join(ln for ln in lines if ln).encode()).hexdigest()
 
 
 def _pmc_rows(d: str) -> dict:
