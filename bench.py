@@ -8,7 +8,8 @@ up 4096->16384, down 16384->4096):
     quantize(X), quantize(W)   amax + scale + cast to row-major FP8 (E4M3)
     Y  = FP8 GEMM (x8, w8 read reduction-major)
     quantize(dY)               (E5M2)
-    dX = FP8 GEMM (dy8, w8),  dW = FP8 GEMM (x8, dy8 both read reduction-major)
+    dX = FP8 GEMM (dy8, w8) and dW = FP8 GEMM (x8, dy8 both read
+    reduction-major), both in one launch (fp8_gemm_pair)
 through the C ABI of libfp8lin.so (the launches fp8_linear_fwd/bwd make),
 with inputs resident in HBM.
 
@@ -51,6 +52,9 @@ def parse():
                     help="JSON file with measured per-launch HBM bytes of the GEMM kernel")
     ap.add_argument("--calibration-copy", type=int, default=0,
                     help="bytes of one plain device copy run before timing (PMC calibration)")
+    ap.add_argument("--step-only", action="store_true",
+                    help="only the warm-up and timed steps (for profiler runs): no breakdown, inference, "
+                         "FP8 weight-gradient, Adam or cold-cache passes")
     return ap.parse_args()
 
 
@@ -114,10 +118,11 @@ def main():
                  lambda: tsf.fp8_gemm(ws.x8, "e4m3", ws.sx, ws.w8, "e4m3", ws.sw, d["Y"], "rows", "cols")),
                 ("quant", f"{n}.dY", 5 * L.M * L.N, 0,
                  lambda: tsf.fp8_quantize(d["dY"], "e5m2", ws.sdy, margin, mu, ws.dy8, transposed=False)),
-                ("gemm", f"{n}.dgrad {L.M}x{L.K}x{L.N}", 0, 2 * L.M * L.K * L.N,
-                 lambda: tsf.fp8_gemm(ws.dy8, "e5m2", ws.sdy, ws.w8, "e4m3", ws.sw, d["dX"])),
-                ("gemm", f"{n}.wgrad {L.K}x{L.N}x{L.M}", 0, 2 * L.K * L.N * L.M,
-                 lambda: tsf.fp8_gemm(ws.x8, "e4m3", ws.sx, ws.dy8, "e5m2", ws.sdy, d["dW"], "cols", "cols")),
+                ("gemm", f"{n}.bwd dgrad {L.M}x{L.K}x{L.N} + wgrad {L.K}x{L.N}x{L.M}", 0, 4 * L.M * L.K * L.N,
+                 lambda: tsf.fp8_gemm_pair(
+                     dict(a=ws.dy8, fa="e5m2", sa=ws.sdy, b=ws.w8, fb="e4m3", sb=ws.sw, out=d["dX"]),
+                     dict(a=ws.x8, fa="e4m3", sa=ws.sx, b=ws.dy8, fb="e5m2", sb=ws.sdy, out=d["dW"],
+                          a_layout="cols", b_layout="cols"))),
             ]
             for kind, label, nbytes, flops, fn in seq:
                 if instrument == "all" or (instrument == "gemm" and kind == "gemm"):
@@ -152,13 +157,15 @@ def main():
     # and cast figures; these events cost a little time, so this pass is
     # kept out of the timed region)
     events.clear()
-    for _ in range(args.breakdown_steps):
-        step("all")
-    torch.cuda.synchronize()
-    brk = [(k, lb, b, f, hip.elapsed_ms(e0, e1)) for k, lb, b, f, e0, e1 in events]
-    infer = inference_pass(tsf, torch, lin, margin, args.steps, args.warmup)
-    fp8dw = fp8_dw_pass(tsf, torch, lin, margin, mu, args.steps, args.warmup)
-    o2 = adam_pass(tsf, torch, lin, margin, mu, args.steps, args.warmup)
+    brk, infer, fp8dw, o2 = [], None, None, None
+    if not args.step_only:
+        for _ in range(args.breakdown_steps):
+            step("all")
+        torch.cuda.synchronize()
+        brk = [(k, lb, b, f, hip.elapsed_ms(e0, e1)) for k, lb, b, f, e0, e1 in events]
+        infer = inference_pass(tsf, torch, lin, margin, args.steps, args.warmup)
+        fp8dw = fp8_dw_pass(tsf, torch, lin, margin, mu, args.steps, args.warmup)
+        o2 = adam_pass(tsf, torch, lin, margin, mu, args.steps, args.warmup)
 
     def aggregate(rows):
         agg = {}
@@ -175,16 +182,17 @@ def main():
     traffic = gemm_traffic(args.traffic)
     roofline = {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": PEAK_FP8_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4), "traffic": traffic,
-                "kernel": "gemm_nt_kernel (FP8 MFMA)",
+                "kernel": "gemm_nt_kernel (forward) + gemm_pair_kernel (dgrad + wgrad), FP8 MFMA",
                 "avg_launch_us": round(g["ms"] * 1e3 / g["n"], 2)}
     agg = aggregate(brk)
     kernels = {}
-    a = agg["quant"]
-    gbs = a["bytes"] / (a["ms"] * 1e-3) / 1e9
-    kernels["amax+cast"] = {"GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
-                            "ms_per_step": round(a["ms"] / args.breakdown_steps, 4),
-                            "avg_call_us": round(a["ms"] * 1e3 / a["n"], 2),
-                            "bytes": "5 per element: amax read 2, cast read 2, row-major FP8 copy 1"}
+    if "quant" in agg:
+        a = agg["quant"]
+        gbs = a["bytes"] / (a["ms"] * 1e-3) / 1e9
+        kernels["amax+cast"] = {"GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
+                                "ms_per_step": round(a["ms"] / args.breakdown_steps, 4),
+                                "avg_call_us": round(a["ms"] * 1e3 / a["n"], 2),
+                                "bytes": "5 per element: amax read 2, cast read 2, row-major FP8 copy 1"}
     kernels["gemm"] = {"TFLOP/s": round(gemm_tflops, 1), "ms_per_step": round(g["ms"] / args.steps, 4)}
     per = {}
     for kind, label, _, fl, t in timed:
@@ -211,7 +219,8 @@ def main():
             e[1] += fl
     kernels["gemm_by_linear"] = {n: {"us_per_step": round(t * 1e3 / args.steps, 1),
                                      "TFLOP/s": round(f / (t * 1e-3) / 1e12, 1)} for n, (t, f) in lt.items()}
-    kernels["amax+cast_cold"] = quantize_cold(tsf, torch, lin, margin, mu, hip)
+    if not args.step_only:
+        kernels["amax+cast_cold"] = quantize_cold(tsf, torch, lin, margin, mu, hip)
     kernels["note"] = ("gemm: events in the timed region; amax+cast (fp8_quantize: amax pass + "
                        f"cast kernel): a separate pass of {args.breakdown_steps} steps with events "
                        "around every call")

@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define FP8LIN_ABI_VERSION 6
+#define FP8LIN_ABI_VERSION 7
 
 typedef enum fp8_fmt {
   FP8_E4M3 = 0, /* OCP E4M3FN: weights and activations [AMAX bullet 4] */
@@ -232,6 +232,36 @@ fp8_status fp8_gemm(const uint8_t* A, fp8_fmt fa, fp8_layout la, const fp8_scale
                     fp8_fmt fb, fp8_layout lb, const fp8_scale_t* sb, int64_t M, int64_t N, int64_t R,
                     void* C_bf16, hipStream_t stream);
 
+/* The arguments of one fp8_gemm call. */
+typedef struct fp8_gemm_args {
+  const uint8_t* A;
+  fp8_fmt fa;
+  fp8_layout la;
+  const fp8_scale_t* sa;
+  const uint8_t* B;
+  fp8_fmt fb;
+  fp8_layout lb;
+  const fp8_scale_t* sb;
+  int64_t M, N, R;
+  void* C;
+} fp8_gemm_args;
+
+/*
+ * a5 + a6 - two GEMMs enqueued together, each computed exactly as fp8_gemm
+ * computes it with the same arguments (same checks and statuses,
+ * bit-identical results). When the pair is a linear's backward - first the
+ * dgrad (A E5M2 ROWS, B E4M3 ROWS), then the wgrad (A E4M3 COLS, B E5M2
+ * COLS) - both run in one kernel launch: the first GEMM's output tiles are
+ * dispatched first and the second's fill its tail, which saves one
+ * launch's ramp-up and drain. Any other pair is launched as two GEMMs in
+ * order.
+ *   first, second: host pointers to the argument sets, read during the
+ *   call only. Both are validated before anything is enqueued (the first
+ *   failing status is returned). The two GEMMs may run concurrently: the
+ *   output of either must not overlap the other's inputs or output.
+ */
+fp8_status fp8_gemm_pair(const fp8_gemm_args* first, const fp8_gemm_args* second, hipStream_t stream);
+
 /*
  * Workspace of one FP8 linear: device pointers owned by the caller.
  *   x8 [M,K], w8 [K,N], dy8 [M,N] (u8, row-major FP8 copies): required.
@@ -268,7 +298,8 @@ fp8_status fp8_linear_fwd(const void* X, const void* W, int64_t M, int64_t K, in
 /*
  * Backward of one linear: fp8_quantize of dY (E5M2, with mu = 2^mu_log2),
  * then dX = dY W^T = gemm(dy8 ROWS, w8 ROWS) and dW = X^T dY =
- * gemm(x8 COLS, dy8 COLS) from the FP8 copies the forward left in ws.
+ * gemm(x8 COLS, dy8 COLS) from the FP8 copies the forward left in ws
+ * (when both are asked for, as one fp8_gemm_pair launch).
  *   dY [M,N] bf16; dX [M,K] bf16 or NULL to skip; dW [K,N] bf16 or NULL to skip.
  */
 fp8_status fp8_linear_bwd(const void* dY, int64_t M, int64_t K, int64_t N, int margin, int mu_log2,

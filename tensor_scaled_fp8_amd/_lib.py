@@ -27,6 +27,7 @@ SIGNATURES = {
     "fp8_cast": (c_int, [c_vp, c_i64, c_i64, c_int, c_vp, c_vp, c_vp, c_vp]),
     "fp8_gemm_nt": (c_int, [c_vp, c_int, c_vp, c_vp, c_int, c_vp, c_i64, c_i64, c_i64, c_vp, c_vp]),
     "fp8_gemm": (c_int, [c_vp, c_int, c_int, c_vp, c_vp, c_int, c_int, c_vp, c_i64, c_i64, c_i64, c_vp, c_vp]),
+    "fp8_gemm_pair": (c_int, [c_vp, c_vp, c_vp]),
     "fp8_linear_fwd": (c_int, [c_vp, c_vp, c_i64, c_i64, c_i64, c_int, c_vp, c_vp, c_vp]),
     "fp8_linear_bwd": (c_int, [c_vp, c_i64, c_i64, c_i64, c_int, c_int, c_vp, c_vp, c_vp, c_vp]),
     "fp8_linear_fwd_cached": (c_int, [c_vp, c_i64, c_i64, c_i64, c_int, c_int, c_vp, c_vp, c_vp, c_vp, c_vp,
@@ -43,13 +44,19 @@ FP8_OPERAND_ROWS, FP8_OPERAND_COLS = 0, 1
 FP8_OK, FP8_ERR_INVALID, FP8_ERR_UNSUPPORTED, FP8_ERR_HIP = 0, 1, 2, 3
 FLAG_NONFINITE, FLAG_ZERO, FLAG_CLAMPED = 1, 2, 4
 FP8_SCALING_AMAX, FP8_SCALING_FIXED = 0, 1
-ABI_VERSION = 6
+ABI_VERSION = 7
 
 
 class LinearWs(ctypes.Structure):
     """fp8_linear_ws: host struct of device pointers."""
     _fields_ = [("x8", c_vp), ("x8t", c_vp), ("w8", c_vp), ("w8t", c_vp), ("dy8", c_vp),
                 ("dy8t", c_vp), ("sx", c_vp), ("sw", c_vp), ("sdy", c_vp)]
+
+
+class GemmArgs(ctypes.Structure):
+    """fp8_gemm_args: the arguments of one fp8_gemm call (host struct)."""
+    _fields_ = [("A", c_vp), ("fa", c_int), ("la", c_int), ("sa", c_vp), ("B", c_vp), ("fb", c_int),
+                ("lb", c_int), ("sb", c_vp), ("M", c_i64), ("N", c_i64), ("R", c_i64), ("C", c_vp)]
 
 
 _lib = None

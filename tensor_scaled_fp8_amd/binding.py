@@ -3,7 +3,7 @@ marshalling only. Torch supplies device memory and the current HIP stream;
 every step of the computation runs in the HIP kernels of libfp8lin.so.
 
 Names follow the C entry points: fp8_amax, fp8_scale, fp8_amax_scale,
-fp8_scale_fixed, fp8_cast, fp8_gemm_nt, fp8_gemm, fp8_quantize, fp8_linear_fwd,
+fp8_scale_fixed, fp8_cast, fp8_gemm_nt, fp8_gemm, fp8_gemm_pair, fp8_quantize, fp8_linear_fwd,
 fp8_linear_bwd, fp8_linear_fwd_cached, fp8_wgrad_fp8, fp8_adam_init_master,
 fp8_adam_step. A scaling record (fp8_scale_t, 64
 bytes) is an int32 tensor of 16 words on the device."""
@@ -16,7 +16,7 @@ import torch
 
 from . import _lib
 from ._lib import (FP8_E4M3, FP8_E5M2, FP8_OPERAND_COLS, FP8_OPERAND_ROWS, FP8_SCALING_AMAX, FP8_SCALING_FIXED,
-                   LinearWs, check, load)
+                   GemmArgs, LinearWs, check, load)
 
 SCALE_WORDS = 16         # sizeof(fp8_scale_t) / 4
 SCALINGS = {"amax": FP8_SCALING_AMAX, "fixed": FP8_SCALING_FIXED}
@@ -148,10 +148,9 @@ def fp8_gemm_nt(a: torch.Tensor, fa, sa: torch.Tensor, b: torch.Tensor, fb, sb: 
 LAYOUTS = {"rows": FP8_OPERAND_ROWS, "cols": FP8_OPERAND_COLS}
 
 
-def fp8_gemm(a: torch.Tensor, fa, sa: torch.Tensor, b: torch.Tensor, fb, sb: torch.Tensor,
-             out: Optional[torch.Tensor] = None, a_layout: str = "rows", b_layout: str = "rows") -> torch.Tensor:
-    """C[M, N] (bf16) = 2^-(bias_a + bias_b) * sum_r A(i, r) B(j, r) on FP8 codes,
-    each operand either "rows" (A [M, R], B [N, R]) or "cols" (A [R, M], B [R, N])."""
+def _gemm_args(a: torch.Tensor, fa, sa: torch.Tensor, b: torch.Tensor, fb, sb: torch.Tensor,
+               out: Optional[torch.Tensor], a_layout: str, b_layout: str):
+    """Shape checks and the fp8_gemm argument set (as a GemmArgs struct)."""
     if a_layout not in LAYOUTS or b_layout not in LAYOUTS:
         raise ValueError("layouts are 'rows' or 'cols'")
     if a.dim() != 2 or b.dim() != 2:
@@ -164,10 +163,33 @@ def fp8_gemm(a: torch.Tensor, fa, sa: torch.Tensor, b: torch.Tensor, fb, sb: tor
         out = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
     if tuple(out.shape) != (M, N):
         raise ValueError("out has the wrong shape")
-    check(load().fp8_gemm(_dev(a, torch.uint8, "A"), _fmt(fa), LAYOUTS[a_layout], _dev(sa, torch.int32, "sa"),
-                          _dev(b, torch.uint8, "B"), _fmt(fb), LAYOUTS[b_layout], _dev(sb, torch.int32, "sb"),
-                          M, N, Ra, _dev(out, torch.bfloat16, "out"), _stream(a)), "fp8_gemm")
+    args = GemmArgs(_dev(a, torch.uint8, "A"), _fmt(fa), LAYOUTS[a_layout], _dev(sa, torch.int32, "sa"),
+                    _dev(b, torch.uint8, "B"), _fmt(fb), LAYOUTS[b_layout], _dev(sb, torch.int32, "sb"),
+                    M, N, Ra, _dev(out, torch.bfloat16, "out"))
+    return args, out
+
+
+def fp8_gemm(a: torch.Tensor, fa, sa: torch.Tensor, b: torch.Tensor, fb, sb: torch.Tensor,
+             out: Optional[torch.Tensor] = None, a_layout: str = "rows", b_layout: str = "rows") -> torch.Tensor:
+    """C[M, N] (bf16) = 2^-(bias_a + bias_b) * sum_r A(i, r) B(j, r) on FP8 codes,
+    each operand either "rows" (A [M, R], B [N, R]) or "cols" (A [R, M], B [R, N])."""
+    g, out = _gemm_args(a, fa, sa, b, fb, sb, out, a_layout, b_layout)
+    check(load().fp8_gemm(g.A, g.fa, g.la, g.sa, g.B, g.fb, g.lb, g.sb, g.M, g.N, g.R, g.C, _stream(a)), "fp8_gemm")
     return out
+
+
+def fp8_gemm_pair(first: dict, second: dict):
+    """Two fp8_gemm calls enqueued together (one launch for a linear's
+    dgrad + wgrad pair); each dict holds fp8_gemm's keyword arguments
+    (a, fa, sa, b, fb, sb, and optionally out, a_layout, b_layout). Returns
+    the two outputs."""
+    def one(d):
+        return _gemm_args(d["a"], d["fa"], d["sa"], d["b"], d["fb"], d["sb"], d.get("out"),
+                          d.get("a_layout", "rows"), d.get("b_layout", "rows"))
+    g0, out0 = one(first)
+    g1, out1 = one(second)
+    check(load().fp8_gemm_pair(ctypes.byref(g0), ctypes.byref(g1), _stream(first["a"])), "fp8_gemm_pair")
+    return out0, out1
 
 
 class LinearWorkspace:

@@ -106,9 +106,9 @@ fp8_status fp8_quantize(const void* x_bf16, int64_t rows, int64_t cols, fp8_fmt 
                                     out_transposed, stream));
 }
 
-fp8_status fp8_gemm(const uint8_t* A, fp8_fmt fa, fp8_layout la, const fp8_scale_t* sa, const uint8_t* B,
-                    fp8_fmt fb, fp8_layout lb, const fp8_scale_t* sb, int64_t M, int64_t N, int64_t R,
-                    void* C_bf16, hipStream_t stream) {
+// the argument checks of fp8_gemm
+static fp8_status check_gemm(const uint8_t* A, int fa, int la, const fp8_scale_t* sa, const uint8_t* B, int fb,
+                             int lb, const fp8_scale_t* sb, int64_t M, int64_t N, int64_t R, const void* C_bf16) {
   if (M < 0 || N < 0 || R < 0 || !fmt_ok(fa) || !fmt_ok(fb)) return FP8_ERR_INVALID;
   if ((la != FP8_OPERAND_ROWS && la != FP8_OPERAND_COLS) || (lb != FP8_OPERAND_ROWS && lb != FP8_OPERAND_COLS))
     return FP8_ERR_INVALID;
@@ -119,8 +119,30 @@ fp8_status fp8_gemm(const uint8_t* A, fp8_fmt fa, fp8_layout la, const fp8_scale
     if (!C_bf16 || !aligned16(C_bf16)) return FP8_ERR_INVALID;
     if (R > 0 && (!A || !B || !aligned16(A) || !aligned16(B))) return FP8_ERR_INVALID;
   }
+  return FP8_OK;
+}
+
+fp8_status fp8_gemm(const uint8_t* A, fp8_fmt fa, fp8_layout la, const fp8_scale_t* sa, const uint8_t* B,
+                    fp8_fmt fb, fp8_layout lb, const fp8_scale_t* sb, int64_t M, int64_t N, int64_t R,
+                    void* C_bf16, hipStream_t stream) {
+  const fp8_status st = check_gemm(A, fa, la, sa, B, fb, lb, sb, M, N, R, C_bf16);
+  if (st != FP8_OK) return st;
   return hip_status(launch_gemm(A, fa, la == FP8_OPERAND_COLS, sa, B, fb, lb == FP8_OPERAND_COLS, sb, M, N, R,
                                 C_bf16, stream));
+}
+
+fp8_status fp8_gemm_pair(const fp8_gemm_args* first, const fp8_gemm_args* second, hipStream_t stream) {
+  if (!first || !second) return FP8_ERR_INVALID;
+  GemmDesc g[2];
+  const fp8_gemm_args* a[2] = {first, second};
+  for (int i = 0; i < 2; ++i) {
+    const fp8_gemm_args& x = *a[i];
+    const fp8_status st = check_gemm(x.A, x.fa, x.la, x.sa, x.B, x.fb, x.lb, x.sb, x.M, x.N, x.R, x.C);
+    if (st != FP8_OK) return st;
+    g[i] = GemmDesc{x.A, (int)x.fa, x.la == FP8_OPERAND_COLS, x.sa, x.B, (int)x.fb, x.lb == FP8_OPERAND_COLS,
+                    x.sb, x.M, x.N, x.R, x.C};
+  }
+  return hip_status(launch_gemm_pair(g[0], g[1], stream));
 }
 
 fp8_status fp8_gemm_nt(const uint8_t* A, fp8_fmt fa, const fp8_scale_t* sa, const uint8_t* B,
@@ -178,14 +200,16 @@ fp8_status fp8_linear_bwd(const void* dY, int64_t M, int64_t K, int64_t N, int m
   if ((e = launch_quantize(dY, M, N, FP8_E5M2, margin, mu_log2, ws->sdy, ws->dy8, ws->dy8t,
                            stream)) != hipSuccess)
     return FP8_ERR_HIP;
-  if (dX && (e = launch_gemm(ws->dy8, FP8_E5M2, false, ws->sdy, ws->w8, FP8_E4M3, false, ws->sw, M, K, N, dX, stream)) !=
-                hipSuccess)
-    return FP8_ERR_HIP;
-  // dW[k, n] = sum_m x8[m, k] dy8[m, n]: both read reduction-major
-  if (dW && (e = launch_gemm(ws->x8, FP8_E4M3, true, ws->sx, ws->dy8, FP8_E5M2, true, ws->sdy, K, N, M, dW, stream)) !=
-                hipSuccess)
-    return FP8_ERR_HIP;
-  return FP8_OK;
+  // dX[m, k] = sum_n dy8[m, n] w8[k, n]; dW[k, n] = sum_m x8[m, k] dy8[m, n]
+  // (both read reduction-major); when both are asked for, one launch
+  const GemmDesc dgrad{ws->dy8, FP8_E5M2, false, ws->sdy, ws->w8, FP8_E4M3, false, ws->sw, M, K, N, dX};
+  const GemmDesc wgrad{ws->x8, FP8_E4M3, true, ws->sx, ws->dy8, FP8_E5M2, true, ws->sdy, K, N, M, dW};
+  if (dX && dW) e = launch_gemm_pair(dgrad, wgrad, stream);
+  else if (dX) e = launch_gemm(dgrad.A, dgrad.fa, dgrad.ta, dgrad.sa, dgrad.B, dgrad.fb, dgrad.tb, dgrad.sb, M, K, N,
+                               dX, stream);
+  else if (dW) e = launch_gemm(wgrad.A, wgrad.fa, wgrad.ta, wgrad.sa, wgrad.B, wgrad.fb, wgrad.tb, wgrad.sb, K, N, M,
+                               dW, stream);
+  return hip_status(e);
 }
 
 fp8_status fp8_linear_fwd_cached(const void* X, int64_t M, int64_t K, int64_t N, int margin,

@@ -118,6 +118,26 @@ hipError_t launch_quantize(const void* x, int64_t rows, int64_t cols, int fmt, i
 hipError_t launch_gemm(const uint8_t* A, int fa, bool ta, const fp8_scale_t* sa, const uint8_t* B, int fb, bool tb,
                        const fp8_scale_t* sb, int64_t M, int64_t N, int64_t R, void* C,
                        hipStream_t st);
+// One GEMM of a pair (the arguments of launch_gemm).
+struct GemmDesc {
+  const uint8_t* A;
+  int fa;
+  bool ta;
+  const fp8_scale_t* sa;
+  const uint8_t* B;
+  int fb;
+  bool tb;
+  const fp8_scale_t* sb;
+  int64_t M, N, R;
+  void* C;
+};
+// true when the pair has a one-launch kernel: the linear backward's dgrad
+// (E5M2 x E4M3, both one row per output index) then its wgrad (E4M3 x
+// E5M2, both reduction-major)
+bool gemm_pair_fused(const GemmDesc& g0, const GemmDesc& g1);
+// both GEMMs, bit-identical to two launch_gemm calls: one launch when
+// gemm_pair_fused, else two
+hipError_t launch_gemm_pair(const GemmDesc& g0, const GemmDesc& g1, hipStream_t st);
 hipError_t launch_gemm_wgrad_amax(const uint8_t* A, bool ta, const fp8_scale_t* sa, const uint8_t* B, bool tb,
                                   const fp8_scale_t* sb, int64_t M, int64_t N, int64_t R, void* C,
                                   fp8_scale_t* s_out, hipStream_t st);

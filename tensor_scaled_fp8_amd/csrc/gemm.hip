@@ -122,6 +122,24 @@ __device__ inline void block_sync_lds() {
   asm volatile("" ::: "memory");
 }
 
+// One GEMM problem: operands, records, sizes and the tile grid.
+struct GemmParams {
+  const uint8_t* A;
+  const uint8_t* B;
+  const fp8_scale_t* sa;
+  const fp8_scale_t* sb;
+  uint16_t* C;
+  int M, N, R, tiles_m, tiles_n;
+};
+
+// The two stage buffers (also the epilogue's staging of C). They are
+// separate LDS objects, always addressed with a compile-time index, so the
+// compiler can tell the buffer being read from the one with loads in flight
+// and does not wait for those. Declared once for the file, so a kernel that
+// runs tiles of two GEMM variants still holds 128 KB.
+__shared__ uint4 g_slot0[kStageBytes / 16];
+__shared__ uint4 g_slot1[kStageBytes / 16];
+
 // AMAX: the epilogue also takes max |C| over the bf16 values it writes and
 // merges (tag << 16) | max into s_out->gen_max (one atomic per block, as the
 // amax pass of fp8_quantize does; tag = s_out->epoch + 1), so a following
@@ -131,25 +149,25 @@ __device__ inline void block_sync_lds() {
 // reduction bytes contiguous (A [M, R], B [N, R]); true: reduction-major
 // (A [R, M], B [R, N]), staged in LDS as [k][output] and turned into MFMA
 // fragments by transposing LDS reads.
+// tile: index of the output tile within the problem's tile grid.
 template <int FA, int FB, bool AMAX, bool TA, bool TB>
-__global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
-    const uint8_t* __restrict__ A, const uint8_t* __restrict__ B, const fp8_scale_t* __restrict__ sa,
-    const fp8_scale_t* __restrict__ sb, int M, int N, int R, uint16_t* __restrict__ C, int tiles_m,
-    int tiles_n, fp8_scale_t* s_out) {
-  // The two stage buffers are separate LDS objects, always addressed with a
-  // compile-time index, so the compiler can tell the buffer being read from
-  // the one with loads in flight and does not wait for those.
-  __shared__ uint4 slot0[kStageBytes / 16], slot1[kStageBytes / 16];
+__device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, fp8_scale_t* s_out) {
+  const uint8_t* __restrict__ A = p.A;
+  const uint8_t* __restrict__ B = p.B;
+  const fp8_scale_t* __restrict__ sa = p.sa;
+  const fp8_scale_t* __restrict__ sb = p.sb;
+  uint16_t* __restrict__ C = p.C;
+  const int M = p.M, N = p.N, R = p.R, tiles_m = p.tiles_m, tiles_n = p.tiles_n;
   auto slot = [&](auto J_) -> lds_u8* {
-    if constexpr ((decltype(J_)::value & 1) == 0) return (lds_u8*)slot0;
-    else return (lds_u8*)slot1;
+    if constexpr ((decltype(J_)::value & 1) == 0) return (lds_u8*)g_slot0;
+    else return (lds_u8*)g_slot1;
   };
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
 
   // ---- tile selection: XCD-contiguous ranges, grouped raster inside ----
   const int nblocks = tiles_m * tiles_n;
-  int pid = blockIdx.x;
+  int pid = tile;
   if ((nblocks & 7) == 0) pid = (pid & 7) * (nblocks >> 3) + (pid >> 3);
   const int per_group = kGroupM * tiles_n;
   const int group = pid / per_group;
@@ -488,7 +506,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
       unsigned long long* word = (unsigned long long*)&s_out->gen_max;
       const unsigned long long seen = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (v > seen) atomicMax(word, v);
-      if (blockIdx.x == 0) s_out->sat_count = 0u;
+      if (tile == 0) s_out->sat_count = 0u;
     }
   } else {
     block_sync_lds();
@@ -531,12 +549,49 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(
   else drain_all(std::false_type{});
 }
 
+// One GEMM: one block per output tile.
+template <int FA, int FB, bool AMAX, bool TA, bool TB>
+__global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(GemmParams p, fp8_scale_t* s_out) {
+  gemm_tile<FA, FB, AMAX, TA, TB>(p, (int)blockIdx.x, s_out);
+}
+
+// Two GEMMs in one launch: blocks below p0's tile count take p0's tiles,
+// the rest p1's, each with the code of its own variant (the first GEMM's
+// tiles are dispatched first). A block does exactly what the single-GEMM
+// kernel's block for that tile does, so the results are bit-identical;
+// one launch instead of two saves the launch ramp and lets the second
+// GEMM's tiles fill the first one's tail. Instantiated for the linear
+// backward: dgrad (E5M2 dy8 x E4M3 w8, both one row per output index) and
+// wgrad (E4M3 x8 x E5M2 dy8, both reduction-major).
+template <int FA0, int FB0, bool TA0, bool TB0, int FA1, int FB1, bool TA1, bool TB1>
+__global__ __launch_bounds__(kThreads, 1) void gemm_pair_kernel(GemmParams p0, GemmParams p1) {
+  const int b = (int)blockIdx.x, n0 = p0.tiles_m * p0.tiles_n;
+  if (b < n0) gemm_tile<FA0, FB0, false, TA0, TB0>(p0, b, nullptr);
+  else gemm_tile<FA1, FB1, false, TA1, TB1>(p1, b - n0, nullptr);
+}
+
+inline GemmParams make_params(const uint8_t* A, const fp8_scale_t* sa, const uint8_t* B, const fp8_scale_t* sb,
+                              int64_t M, int64_t N, int64_t R, void* C) {
+  GemmParams p;
+  p.A = A;
+  p.B = B;
+  p.sa = sa;
+  p.sb = sb;
+  p.C = (uint16_t*)C;
+  p.M = (int)M;
+  p.N = (int)N;
+  p.R = (int)R;
+  p.tiles_m = (int)((M + kBM - 1) / kBM);
+  p.tiles_n = (int)((N + kBN - 1) / kBN);
+  return p;
+}
+
 template <int FA, int FB, bool AMAX, bool TA, bool TB>
 hipError_t launch_typed(const uint8_t* A, const fp8_scale_t* sa, const uint8_t* B, const fp8_scale_t* sb,
                         int64_t M, int64_t N, int64_t R, void* C, hipStream_t st, fp8_scale_t* s_out) {
-  const int tiles_m = (int)((M + kBM - 1) / kBM), tiles_n = (int)((N + kBN - 1) / kBN);
-  hipLaunchKernelGGL((gemm_nt_kernel<FA, FB, AMAX, TA, TB>), dim3(tiles_m * tiles_n), dim3(kThreads), 0, st, A,
-                     B, sa, sb, (int)M, (int)N, (int)R, (uint16_t*)C, tiles_m, tiles_n, s_out);
+  const GemmParams p = make_params(A, sa, B, sb, M, N, R, C);
+  hipLaunchKernelGGL((gemm_nt_kernel<FA, FB, AMAX, TA, TB>), dim3(p.tiles_m * p.tiles_n), dim3(kThreads), 0, st,
+                     p, s_out);
   return hipGetLastError();
 }
 
@@ -558,6 +613,29 @@ hipError_t launch_gemm(const uint8_t* A, int fa, bool ta, const fp8_scale_t* sa,
   if (fa == FP8_E5M2 && fb == FP8_E4M3) return launch_layouts<1, 0>(A, ta, sa, B, tb, sb, M, N, R, C, st);
   if (fa == FP8_E4M3 && fb == FP8_E5M2) return launch_layouts<0, 1>(A, ta, sa, B, tb, sb, M, N, R, C, st);
   return launch_layouts<1, 1>(A, ta, sa, B, tb, sb, M, N, R, C, st);
+}
+
+bool gemm_pair_fused(const GemmDesc& g0, const GemmDesc& g1) {
+  return g0.fa == FP8_E5M2 && g0.fb == FP8_E4M3 && !g0.ta && !g0.tb && g1.fa == FP8_E4M3 && g1.fb == FP8_E5M2 &&
+         g1.ta && g1.tb;
+}
+
+hipError_t launch_gemm_pair(const GemmDesc& g0, const GemmDesc& g1, hipStream_t st) {
+  const bool e0 = g0.M == 0 || g0.N == 0, e1 = g1.M == 0 || g1.N == 0;
+  if (e0 || e1 || !gemm_pair_fused(g0, g1)) {
+    hipError_t e = hipSuccess;
+    if (!e0) e = launch_gemm(g0.A, g0.fa, g0.ta, g0.sa, g0.B, g0.fb, g0.tb, g0.sb, g0.M, g0.N, g0.R, g0.C, st);
+    if (e == hipSuccess && !e1)
+      e = launch_gemm(g1.A, g1.fa, g1.ta, g1.sa, g1.B, g1.fb, g1.tb, g1.sb, g1.M, g1.N, g1.R, g1.C, st);
+    return e;
+  }
+  constexpr int E4 = FP8_E4M3, E5 = FP8_E5M2;
+  const GemmParams p0 = make_params(g0.A, g0.sa, g0.B, g0.sb, g0.M, g0.N, g0.R, g0.C);
+  const GemmParams p1 = make_params(g1.A, g1.sa, g1.B, g1.sb, g1.M, g1.N, g1.R, g1.C);
+  const int blocks = p0.tiles_m * p0.tiles_n + p1.tiles_m * p1.tiles_n;
+  hipLaunchKernelGGL((gemm_pair_kernel<E5, E4, false, false, E4, E5, true, true>), dim3(blocks), dim3(kThreads), 0,
+                     st, p0, p1);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm_wgrad_amax(const uint8_t* A, bool ta, const fp8_scale_t* sa, const uint8_t* B, bool tb,

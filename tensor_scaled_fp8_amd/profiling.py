@@ -55,7 +55,7 @@ def kernel_stats(d: str) -> dict:
 def _short(name: str) -> str:
     """Kernel name without namespaces and parameter list; template arguments
     kept (they select formats, layouts and variants)."""
-    for key in ("gemm_nt_kernel<", "cast_kernel<"):
+    for key in ("gemm_nt_kernel<", "gemm_pair_kernel<", "cast_kernel<"):
         if key in name:
             return name[name.index(key):].split(">")[0] + ">"
     base = name.replace("(anonymous namespace)::", "")
@@ -96,7 +96,7 @@ def traffic(fetch_dir: str, write_dir: str, kernel: str, copy_bytes: int) -> dic
         if not copies:
             raise RuntimeError(f"no copy dispatch in {d}")
         factor = copy_bytes / (max(copies) * 1024.0)
-        vals = [v for n, v in per.values() if kernel in n]
+        vals = [v for n, v in per.values() if any(k in n for k in kernel.split(","))]
         if not vals:
             raise RuntimeError(f"no dispatch of {kernel} in {d}")
         out[f"{key}_kib_per_dispatch_raw"] = sum(vals) / len(vals)
@@ -187,9 +187,10 @@ def mfma_markdown(d: str, command: str) -> str:
     rows = _pmc_rows(d)
     groups = defaultdict(list)
     for e in rows.values():
-        if "gemm_nt_kernel" not in e["name"]:
+        key = next((k for k in ("gemm_nt_kernel<", "gemm_pair_kernel<") if k in e["name"]), None)
+        if key is None:
             continue
-        tmpl = e["name"][e["name"].index("gemm_nt_kernel<"):].split(">")[0] + ">"
+        tmpl = e["name"][e["name"].index(key):].split(">")[0] + ">"
         groups[(tmpl, e["grid"] // 256)].append(e)
     lines = ["# FP8 MFMA utilisation and shader clock of the GEMM kernel, GPT-7B-style layer", "",
              "Command:", "", "```", command, "```", "",
@@ -229,7 +230,8 @@ def main():
     b = sub.add_parser("traffic")
     b.add_argument("--fetch", required=True)
     b.add_argument("--write", required=True)
-    b.add_argument("--kernel", default="gemm_nt_kernel")
+    b.add_argument("--kernel", default="gemm_nt_kernel,gemm_pair_kernel",
+                   help="comma-separated kernel name parts; dispatches of any of them are averaged")
     b.add_argument("--copy-bytes", type=int, required=True)
     b.add_argument("--command", default="")
     b.add_argument("--out")

@@ -31,7 +31,7 @@ def test_header_functions_all_exported():
     for n in names:
         assert hasattr(lib, n), n
         assert n in _lib.SIGNATURES, f"binding lacks {n}"
-    assert lib.fp8_abi_version() == 6
+    assert lib.fp8_abi_version() == 7
 
 
 def test_status_strings():
@@ -101,6 +101,21 @@ def test_argument_validation_without_launch():
     assert gl(_vp(ok), 0, 0, _vp(ok), _vp(ok), 0, -1, _vp(ok), 16, 16, 16, _vp(ok), None) == INV
     assert gl(_vp(ok), 0, 1, _vp(ok), _vp(ok), 0, 1, _vp(ok), 16, 16, 40, _vp(ok), None) == UNS
     assert gl(_vp(ok), 0, 1, _vp(ok), None, 0, 1, _vp(ok), 16, 16, 16, _vp(ok), None) == INV
+    # gemm pair: each argument set checked as fp8_gemm checks it, nothing enqueued on failure
+    gp = lib.fp8_gemm_pair
+    good = _lib.GemmArgs(ok, 1, 0, ok, ok, 0, 0, ok, 16, 16, 16, ok)
+    assert gp(None, ctypes.byref(good), None) == INV
+    assert gp(ctypes.byref(good), None, None) == INV
+    bad_fmt = _lib.GemmArgs(ok, 2, 0, ok, ok, 0, 0, ok, 16, 16, 16, ok)
+    assert gp(ctypes.byref(good), ctypes.byref(bad_fmt), None) == INV
+    bad_layout = _lib.GemmArgs(ok, 0, 3, ok, ok, 1, 1, ok, 16, 16, 16, ok)
+    assert gp(ctypes.byref(bad_layout), ctypes.byref(good), None) == INV
+    ragged = _lib.GemmArgs(ok, 0, 1, ok, ok, 1, 1, ok, 16, 16, 40, ok)
+    assert gp(ctypes.byref(good), ctypes.byref(ragged), None) == UNS
+    misaligned = _lib.GemmArgs(ok, 0, 1, ok, ok, 1, 1, ok, 16, 16, 16, ok + 2)
+    assert gp(ctypes.byref(good), ctypes.byref(misaligned), None) == INV
+    no_rec = _lib.GemmArgs(ok, 0, 1, None, ok, 1, 1, ok, 16, 16, 16, ok)
+    assert gp(ctypes.byref(no_rec), ctypes.byref(good), None) == INV
     # linear: workspace checks
     ws = _lib.LinearWs(ok, ok, ok, ok, ok, ok, ok, ok, ok)
     assert lib.fp8_linear_fwd(_vp(ok), _vp(ok), 16, 16, 16, 0, None, _vp(ok), None) == INV
