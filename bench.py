@@ -5,7 +5,8 @@ linears, forward + backward, on one MI355X.
 A step runs, for every linear of the layer (default: the GPT-7B-style
 layer, 4096 tokens, hidden 4096: qkv 4096->12288, proj 4096->4096,
 up 4096->16384, down 16384->4096):
-    quantize(X), quantize(W)   amax + scale + cast to row-major FP8 (E4M3)
+    quantize(X), quantize(W)   amax + scale + cast to row-major FP8 (E4M3),
+                               both tensors in one launch pair (fp8_quantize_batch)
     Y  = FP8 GEMM (x8, w8 read reduction-major)
     quantize(dY)               (E5M2)
     dX = FP8 GEMM (dy8, w8) and dW = FP8 GEMM (x8, dy8 both read
@@ -110,10 +111,10 @@ def main():
             # amax + cast to the row-major FP8 copy (2 B read twice, 1 B written);
             # the GEMMs read those copies, reduction-major where needed
             seq = [
-                ("quant", f"{n}.X", 5 * L.M * L.K, 0,
-                 lambda: tsf.fp8_quantize(d["X"], "e4m3", ws.sx, margin, 0, ws.x8, transposed=False)),
-                ("quant", f"{n}.W", 5 * L.K * L.N, 0,
-                 lambda: tsf.fp8_quantize(d["W"], "e4m3", ws.sw, margin, 0, ws.w8, transposed=False)),
+                ("quant", f"{n}.X+W", 5 * (L.M * L.K + L.K * L.N), 0,
+                 lambda: tsf.fp8_quantize_batch([
+                     dict(x=d["X"], fmt="e4m3", s=ws.sx, margin=margin, out_row=ws.x8, transposed=False),
+                     dict(x=d["W"], fmt="e4m3", s=ws.sw, margin=margin, out_row=ws.w8, transposed=False)])),
                 ("gemm", f"{n}.fwd {L.M}x{L.N}x{L.K}", 0, 2 * L.M * L.N * L.K,
                  lambda: tsf.fp8_gemm(ws.x8, "e4m3", ws.sx, ws.w8, "e4m3", ws.sw, d["Y"], "rows", "cols")),
                 ("quant", f"{n}.dY", 5 * L.M * L.N, 0,

@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define FP8LIN_ABI_VERSION 7
+#define FP8LIN_ABI_VERSION 8
 
 typedef enum fp8_fmt {
   FP8_E4M3 = 0, /* OCP E4M3FN: weights and activations [AMAX bullet 4] */
@@ -166,6 +166,37 @@ int32_t fp8_bias_host(float amax, fp8_fmt fmt, int margin, int mu_log2, uint32_t
 fp8_status fp8_quantize(const void* x_bf16, int64_t rows, int64_t cols, fp8_fmt fmt, int margin,
                         int mu_log2, fp8_scale_t* s_dev, uint8_t* out_rowwise, uint8_t* out_transposed,
                         hipStream_t stream);
+
+/* Most tensors one fp8_quantize_batch call takes. */
+#define FP8_QUANTIZE_BATCH_MAX 4
+
+/* The arguments of one fp8_quantize call. */
+typedef struct fp8_quantize_args {
+  const void* x;             /* bf16 [rows, cols], device */
+  int64_t rows, cols;
+  fp8_fmt fmt;
+  int margin, mu_log2;
+  fp8_scale_t* s;            /* the tensor's own record (device) */
+  uint8_t* out_rowwise;      /* nullable */
+  uint8_t* out_transposed;   /* nullable */
+} fp8_quantize_args;
+
+/*
+ * a1 + a2 + a3 for up to FP8_QUANTIZE_BATCH_MAX tensors in two kernel
+ * launches (one amax pass over all of them, then all their casts), each
+ * tensor with its own per-tensor scale exactly as fp8_quantize computes it
+ * (same record fields, bit-identical FP8 bytes). For tensors that are ready
+ * together, such as a linear's X and W before its forward GEMM: one launch
+ * pair instead of one per tensor, whose grids share the chip in
+ * proportion to the tensors' sizes.
+ *   tensors: host array of count argument sets, read during the call only;
+ *   1 <= count <= FP8_QUANTIZE_BATCH_MAX, else FP8_ERR_INVALID. Each set
+ *   is checked as fp8_quantize checks its arguments (the first failing
+ *   status is returned, nothing enqueued). The records must be distinct
+ *   (FP8_ERR_INVALID otherwise); no output may overlap another tensor's
+ *   input, output or record.
+ */
+fp8_status fp8_quantize_batch(const fp8_quantize_args* tensors, int count, hipStream_t stream);
 
 /*
  * FP8-CSCALE fixed scaling [AMAX "Proposed method" bullet 6, "Main results"
@@ -294,6 +325,8 @@ typedef struct fp8_linear_ws {
  */
 fp8_status fp8_linear_fwd(const void* X, const void* W, int64_t M, int64_t K, int64_t N, int margin,
                           const fp8_linear_ws* ws, void* Y, hipStream_t stream);
+/* (X and W are quantised together, as one fp8_quantize_batch: ws->sx and
+ * ws->sw must be distinct records, else FP8_ERR_INVALID.) */
 
 /*
  * Backward of one linear: fp8_quantize of dY (E5M2, with mu = 2^mu_log2),

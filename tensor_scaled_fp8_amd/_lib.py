@@ -23,6 +23,7 @@ SIGNATURES = {
     "fp8_amax_scale": (c_int, [c_vp, c_i64, c_int, c_int, c_int, c_vp, c_vp]),
     "fp8_bias_host": (ctypes.c_int32, [ctypes.c_float, c_int, c_int, c_int, ctypes.POINTER(ctypes.c_uint32)]),
     "fp8_quantize": (c_int, [c_vp, c_i64, c_i64, c_int, c_int, c_int, c_vp, c_vp, c_vp, c_vp]),
+    "fp8_quantize_batch": (c_int, [c_vp, c_int, c_vp]),
     "fp8_scale_fixed": (c_int, [c_vp, ctypes.c_int32, c_vp]),
     "fp8_cast": (c_int, [c_vp, c_i64, c_i64, c_int, c_vp, c_vp, c_vp, c_vp]),
     "fp8_gemm_nt": (c_int, [c_vp, c_int, c_vp, c_vp, c_int, c_vp, c_i64, c_i64, c_i64, c_vp, c_vp]),
@@ -44,13 +45,22 @@ FP8_OPERAND_ROWS, FP8_OPERAND_COLS = 0, 1
 FP8_OK, FP8_ERR_INVALID, FP8_ERR_UNSUPPORTED, FP8_ERR_HIP = 0, 1, 2, 3
 FLAG_NONFINITE, FLAG_ZERO, FLAG_CLAMPED = 1, 2, 4
 FP8_SCALING_AMAX, FP8_SCALING_FIXED = 0, 1
-ABI_VERSION = 7
+ABI_VERSION = 8
 
 
 class LinearWs(ctypes.Structure):
     """fp8_linear_ws: host struct of device pointers."""
     _fields_ = [("x8", c_vp), ("x8t", c_vp), ("w8", c_vp), ("w8t", c_vp), ("dy8", c_vp),
                 ("dy8t", c_vp), ("sx", c_vp), ("sw", c_vp), ("sdy", c_vp)]
+
+
+class QuantizeArgs(ctypes.Structure):
+    """fp8_quantize_args: the arguments of one fp8_quantize call (host struct)."""
+    _fields_ = [("x", c_vp), ("rows", c_i64), ("cols", c_i64), ("fmt", c_int), ("margin", c_int),
+                ("mu_log2", c_int), ("s", c_vp), ("out_rowwise", c_vp), ("out_transposed", c_vp)]
+
+
+QUANTIZE_BATCH_MAX = 4
 
 
 class GemmArgs(ctypes.Structure):

@@ -3,7 +3,8 @@ marshalling only. Torch supplies device memory and the current HIP stream;
 every step of the computation runs in the HIP kernels of libfp8lin.so.
 
 Names follow the C entry points: fp8_amax, fp8_scale, fp8_amax_scale,
-fp8_scale_fixed, fp8_cast, fp8_gemm_nt, fp8_gemm, fp8_gemm_pair, fp8_quantize, fp8_linear_fwd,
+fp8_scale_fixed, fp8_cast, fp8_gemm_nt, fp8_gemm, fp8_gemm_pair, fp8_quantize, fp8_quantize_batch,
+fp8_linear_fwd,
 fp8_linear_bwd, fp8_linear_fwd_cached, fp8_wgrad_fp8, fp8_adam_init_master,
 fp8_adam_step. A scaling record (fp8_scale_t, 64
 bytes) is an int32 tensor of 16 words on the device."""
@@ -16,7 +17,7 @@ import torch
 
 from . import _lib
 from ._lib import (FP8_E4M3, FP8_E5M2, FP8_OPERAND_COLS, FP8_OPERAND_ROWS, FP8_SCALING_AMAX, FP8_SCALING_FIXED,
-                   GemmArgs, LinearWs, check, load)
+                   GemmArgs, LinearWs, QuantizeArgs, check, load)
 
 SCALE_WORDS = 16         # sizeof(fp8_scale_t) / 4
 SCALINGS = {"amax": FP8_SCALING_AMAX, "fixed": FP8_SCALING_FIXED}
@@ -126,6 +127,35 @@ def fp8_quantize(x: torch.Tensor, fmt, s: torch.Tensor, margin: int = 0, mu_log2
                               _dev(s, torch.int32, "s"), _dev(out_row, torch.uint8, "out_row"),
                               _dev(out_t, torch.uint8, "out_t"), _stream(x)), "fp8_quantize")
     return out_row, out_t
+
+
+def fp8_quantize_batch(tensors):
+    """fp8_quantize of up to 4 tensors in two launches (one amax pass over
+    all, then all casts), each with its own record. tensors: list of dicts
+    with fp8_quantize's keyword arguments (x, fmt, s, and optionally margin,
+    mu_log2, out_row, out_t, rowwise, transposed). Returns a list of
+    (rowwise or None, transposed or None)."""
+    n = len(tensors)
+    if not 1 <= n <= _lib.QUANTIZE_BATCH_MAX:
+        raise ValueError(f"1 to {_lib.QUANTIZE_BATCH_MAX} tensors per batch")
+    args = (QuantizeArgs * n)()
+    outs = []
+    for i, d in enumerate(tensors):
+        x = d["x"]
+        if x.dim() != 2:
+            raise ValueError("x must be 2-D")
+        rows, cols = x.shape
+        out_row, out_t = d.get("out_row"), d.get("out_t")
+        if d.get("rowwise", True) and out_row is None:
+            out_row = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+        if d.get("transposed", True) and out_t is None:
+            out_t = torch.empty((cols, rows), dtype=torch.uint8, device=x.device)
+        args[i] = QuantizeArgs(_dev(x, torch.bfloat16, "x"), rows, cols, _fmt(d["fmt"]), d.get("margin", 0),
+                               d.get("mu_log2", 0), _dev(d["s"], torch.int32, "s"),
+                               _dev(out_row, torch.uint8, "out_row"), _dev(out_t, torch.uint8, "out_t"))
+        outs.append((out_row, out_t))
+    check(load().fp8_quantize_batch(args, n, _stream(tensors[0]["x"])), "fp8_quantize_batch")
+    return outs
 
 
 def fp8_gemm_nt(a: torch.Tensor, fa, sa: torch.Tensor, b: torch.Tensor, fb, sb: torch.Tensor,

@@ -60,13 +60,13 @@ __device__ inline void write_scale(fp8_scale_t* s, uint32_t mag, bool fuse, int 
   s->flags = flags;
 }
 
-// Block-wide max of |x| bits over this block's contiguous chunk (block-
-// contiguous chunks of whole kUnroll*256-vector steps; block 0 also takes
+// Block-wide max of |x| bits over chunk blk of the tensor (block-
+// contiguous chunks of whole kUnroll*256-vector steps; chunk 0 also takes
 // the < 8-element tail). The result is valid in thread 0.
 __device__ inline uint32_t block_max_bits(const u32x4* __restrict__ x, int64_t n_vec, int64_t per_block,
-                                          const uint16_t* __restrict__ tail, int tail_n) {
+                                          const uint16_t* __restrict__ tail, int tail_n, int blk) {
   u16x2 m = {0, 0};
-  const int64_t b0 = (int64_t)blockIdx.x * per_block;
+  const int64_t b0 = (int64_t)blk * per_block;
   const int64_t b1 = b0 + per_block < n_vec ? b0 + per_block : n_vec;
   int64_t base = b0;
   for (; base + kUnroll * kThreads <= b1; base += kUnroll * kThreads) {
@@ -88,7 +88,7 @@ __device__ inline uint32_t block_max_bits(const u32x4* __restrict__ x, int64_t n
     m = vmax(m, v.z);
     m = vmax(m, v.w);
   }
-  if (blockIdx.x == 0 && (int)threadIdx.x < tail_n) {
+  if (blk == 0 && (int)threadIdx.x < tail_n) {
     m = vmax(m, (uint32_t)tail[threadIdx.x]);
   }
   uint32_t r = m.x > m.y ? m.x : m.y;
@@ -107,17 +107,46 @@ __device__ inline uint32_t block_max_bits(const u32x4* __restrict__ x, int64_t n
   return b;
 }
 
+// merge (tag << 16) | b into the record's tagged maximum (see above)
+__device__ inline void merge_max(fp8_scale_t* s, uint32_t b) {
+  const unsigned long long v = (reduction_tag(s) << 16) | b;
+  unsigned long long* word = (unsigned long long*)&s->gen_max;
+  const unsigned long long seen = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (v > seen) atomicMax(word, v);
+}
+
 __global__ __launch_bounds__(kThreads) void amax_gen_kernel(const u32x4* __restrict__ x, int64_t n_vec,
                                                             int64_t per_block,
                                                             const uint16_t* __restrict__ tail,
                                                             int tail_n, fp8_scale_t* s) {
-  const uint32_t b = block_max_bits(x, n_vec, per_block, tail, tail_n);
-  if (threadIdx.x == 0) {
-    const unsigned long long v = (reduction_tag(s) << 16) | b;
-    unsigned long long* word = (unsigned long long*)&s->gen_max;
-    const unsigned long long seen = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (v > seen) atomicMax(word, v);
-  }
+  const uint32_t b = block_max_bits(x, n_vec, per_block, tail, tail_n, (int)blockIdx.x);
+  if (threadIdx.x == 0) merge_max(s, b);
+}
+
+// amax passes of up to kQuantBatchMax tensors in one launch: blocks
+// first_block[i] .. first_block[i+1]-1 sweep tensor i's chunks and merge
+// into its record, exactly as amax_gen_kernel's blocks would.
+struct AmaxEntry {
+  const u32x4* x;
+  int64_t n_vec, per_block;
+  const uint16_t* tail;
+  fp8_scale_t* s;
+  int tail_n, first_block;
+};
+struct AmaxBatch {
+  AmaxEntry e[kQuantBatchMax];
+  int count;
+};
+
+__global__ __launch_bounds__(kThreads) void amax_batch_kernel(AmaxBatch bt) {
+  const int blk = (int)blockIdx.x;
+  int i = 0;
+#pragma unroll
+  for (int k = 1; k < kQuantBatchMax; ++k)
+    if (k < bt.count && blk >= bt.e[k].first_block) i = k;
+  const AmaxEntry& e = bt.e[i];
+  const uint32_t b = block_max_bits(e.x, e.n_vec, e.per_block, e.tail, e.tail_n, blk - e.first_block);
+  if (threadIdx.x == 0) merge_max(e.s, b);
 }
 
 // fp8_amax / fp8_amax_scale: publish the maximum the reduction just merged
@@ -171,15 +200,16 @@ struct SweepGrid {
   int tail_n;
   const uint16_t* tail;
 };
-// enough blocks to fill the chip, each a contiguous chunk of whole steps
-SweepGrid sweep_grid(const void* x, int64_t n) {
+// enough blocks to fill the chip (at most max_blocks), each a contiguous
+// chunk of whole steps
+SweepGrid sweep_grid(const void* x, int64_t n, int64_t max_blocks = kMaxBlocks) {
   SweepGrid g;
   g.n_vec = n / 8;
   g.tail_n = (int)(n - g.n_vec * 8);
   g.tail = (const uint16_t*)x + g.n_vec * 8;
   const int64_t step = (int64_t)kThreads * kUnroll;
   int64_t blocks = (g.n_vec + step - 1) / step;
-  blocks = blocks < 1 ? 1 : (blocks > kMaxBlocks ? kMaxBlocks : blocks);
+  blocks = blocks < 1 ? 1 : (blocks > max_blocks ? max_blocks : blocks);
   g.per_block = ((g.n_vec + blocks - 1) / blocks + step - 1) / step * step;
   g.blocks = g.n_vec > 0 ? (g.n_vec + g.per_block - 1) / g.per_block : 1;
   return g;
@@ -190,6 +220,32 @@ hipError_t launch_amax_gen(const void* x, int64_t n, fp8_scale_t* s, hipStream_t
   const SweepGrid g = sweep_grid(x, n);
   hipLaunchKernelGGL(amax_gen_kernel, dim3((unsigned)g.blocks), dim3(kThreads), 0, st, (const u32x4*)x,
                      g.n_vec, g.per_block, g.tail, g.tail_n, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_amax_batch(const QuantDesc* d, int count, hipStream_t st) {
+  if (count < 1 || count > kQuantBatchMax) return hipErrorInvalidValue;
+  // the chip-filling block budget of one sweep, shared in proportion to size
+  int64_t total = 0;
+  for (int i = 0; i < count; ++i) total += d[i].rows * d[i].cols;
+  AmaxBatch bt{};
+  bt.count = count;
+  int blocks = 0;
+  for (int i = 0; i < count; ++i) {
+    const int64_t n = d[i].rows * d[i].cols;
+    const int64_t cap = total > 0 ? (kMaxBlocks * n + total - 1) / total : 1;
+    const SweepGrid g = sweep_grid(d[i].x, n, cap < 1 ? 1 : cap);
+    AmaxEntry& e = bt.e[i];
+    e.x = (const u32x4*)d[i].x;
+    e.n_vec = g.n_vec;
+    e.per_block = g.per_block;
+    e.tail = g.tail;
+    e.tail_n = g.tail_n;
+    e.s = d[i].s;
+    e.first_block = blocks;
+    blocks += (int)g.blocks;
+  }
+  hipLaunchKernelGGL(amax_batch_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, st, bt);
   return hipGetLastError();
 }
 

@@ -90,9 +90,10 @@ fp8_status fp8_cast(const void* x_bf16, int64_t rows, int64_t cols, fp8_fmt fmt,
   return hip_status(launch_cast(x_bf16, rows, cols, fmt, s_dev, out_rowwise, out_transposed, stream));
 }
 
-fp8_status fp8_quantize(const void* x_bf16, int64_t rows, int64_t cols, fp8_fmt fmt, int margin,
-                        int mu_log2, fp8_scale_t* s_dev, uint8_t* out_rowwise, uint8_t* out_transposed,
-                        hipStream_t stream) {
+// the argument checks of fp8_quantize
+static fp8_status check_quantize(const void* x_bf16, int64_t rows, int64_t cols, int fmt, int margin, int mu_log2,
+                                 const fp8_scale_t* s_dev, const uint8_t* out_rowwise,
+                                 const uint8_t* out_transposed) {
   if (rows < 0 || cols < 0 || !fmt_ok(fmt) || !int_ok(margin) || !int_ok(mu_log2) || !s_dev ||
       !aligned16(s_dev))
     return FP8_ERR_INVALID;
@@ -102,8 +103,32 @@ fp8_status fp8_quantize(const void* x_bf16, int64_t rows, int64_t cols, fp8_fmt 
     if (out_rowwise && !aligned16(out_rowwise)) return FP8_ERR_INVALID;
     if (out_transposed && !aligned16(out_transposed)) return FP8_ERR_INVALID;
   }
+  return FP8_OK;
+}
+
+fp8_status fp8_quantize(const void* x_bf16, int64_t rows, int64_t cols, fp8_fmt fmt, int margin,
+                        int mu_log2, fp8_scale_t* s_dev, uint8_t* out_rowwise, uint8_t* out_transposed,
+                        hipStream_t stream) {
+  const fp8_status st = check_quantize(x_bf16, rows, cols, fmt, margin, mu_log2, s_dev, out_rowwise, out_transposed);
+  if (st != FP8_OK) return st;
   return hip_status(launch_quantize(x_bf16, rows, cols, fmt, margin, mu_log2, s_dev, out_rowwise,
                                     out_transposed, stream));
+}
+
+fp8_status fp8_quantize_batch(const fp8_quantize_args* tensors, int count, hipStream_t stream) {
+  if (!tensors || count < 1 || count > FP8_QUANTIZE_BATCH_MAX) return FP8_ERR_INVALID;
+  static_assert(FP8_QUANTIZE_BATCH_MAX == kQuantBatchMax, "batch limit");
+  QuantDesc d[kQuantBatchMax];
+  for (int i = 0; i < count; ++i) {
+    const fp8_quantize_args& a = tensors[i];
+    const fp8_status st = check_quantize(a.x, a.rows, a.cols, a.fmt, a.margin, a.mu_log2, a.s, a.out_rowwise,
+                                         a.out_transposed);
+    if (st != FP8_OK) return st;
+    for (int k = 0; k < i; ++k)
+      if (tensors[k].s == a.s) return FP8_ERR_INVALID;  // one record per tensor
+    d[i] = QuantDesc{a.x, a.rows, a.cols, (int)a.fmt, a.margin, a.mu_log2, a.s, a.out_rowwise, a.out_transposed};
+  }
+  return hip_status(launch_quantize_batch(d, count, stream));
 }
 
 // the argument checks of fp8_gemm
@@ -176,12 +201,11 @@ fp8_status fp8_linear_fwd(const void* X, const void* W, int64_t M, int64_t K, in
   if ((M * K > 0 && (!X || !aligned16(X))) || (K * N > 0 && (!W || !aligned16(W))) ||
       (M * N > 0 && (!Y || !aligned16(Y))))
     return FP8_ERR_INVALID;
-  if (launch_quantize(X, M, K, FP8_E4M3, margin, 0, ws->sx, ws->x8, ws->x8t, stream) !=
-      hipSuccess)
-    return FP8_ERR_HIP;
-  if (launch_quantize(W, K, N, FP8_E4M3, margin, 0, ws->sw, ws->w8, ws->w8t, stream) !=
-      hipSuccess)
-    return FP8_ERR_HIP;
+  if (ws->sx == ws->sw) return FP8_ERR_INVALID;
+  // X and W in one amax launch and one cast launch
+  const QuantDesc q[2] = {QuantDesc{X, M, K, FP8_E4M3, margin, 0, ws->sx, ws->x8, ws->x8t},
+                          QuantDesc{W, K, N, FP8_E4M3, margin, 0, ws->sw, ws->w8, ws->w8t}};
+  if (launch_quantize_batch(q, 2, stream) != hipSuccess) return FP8_ERR_HIP;
   // Y[m, n] = sum_k x8[m, k] w8[k, n]: w8 read reduction-major
   return hip_status(launch_gemm(ws->x8, FP8_E4M3, false, ws->sx, ws->w8, FP8_E4M3, true, ws->sw, M, N, K, Y, stream));
 }

@@ -76,6 +76,11 @@ __device__ inline void transpose4(const uint32_t in[4], uint32_t out[4]) {
   out[3] = __builtin_amdgcn_perm(b1, a1, 0x07060302u);
 }
 
+// LDS of a cast block, declared once for the file so that a kernel holding
+// both format variants (the batch kernel) still needs only this much.
+__shared__ uint4 g_tile[kTile * kTile / 16];  // transposed tile: 128 rows of 128 bytes
+__shared__ uint32_t g_wsum[kThreads / 64];    // COUNT: per-wave sums
+
 // DERIVE = false: the scale comes from the record's published fields.
 // DERIVE = true (fp8_quantize): every block derives it from the record's
 // tagged maximum, which the amax pass just merged, with the same rule as
@@ -84,15 +89,14 @@ __device__ inline void transpose4(const uint32_t in[4], uint32_t out[4]) {
 // COUNT (with DERIVE): also count the elements whose scaled magnitude
 // exceeds the format's max (inf included, NaN not) into s->sat_count, which
 // the kernel before this one cleared.
-template <int FMT, bool DERIVE, bool COUNT = false>
-__global__ __launch_bounds__(kThreads) void cast_kernel(const uint16_t* __restrict__ x, int64_t rows,
-                                                        int64_t cols, int64_t tiles_c, fp8_scale_t* s,
-                                                        uint8_t* __restrict__ out_row,
-                                                        uint8_t* __restrict__ out_t, int margin,
-                                                        int mu_log2) {
-  __shared__ uint4 lds[kTile * kTile / 16];  // transposed tile: 128 rows of 128 bytes
+// tile: index of the 128 x 128 tile within the tensor (row-major over tiles).
+template <int FMT, bool DERIVE, bool COUNT>
+__device__ __forceinline__ void cast_tile(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
+                                          int64_t tiles_c, fp8_scale_t* s, uint8_t* __restrict__ out_row,
+                                          uint8_t* __restrict__ out_t, int margin, int mu_log2, int64_t tile) {
+  uint4* const lds = g_tile;
   const int t = threadIdx.x;
-  const int64_t tr = blockIdx.x / tiles_c, tc = blockIdx.x - (blockIdx.x / tiles_c) * tiles_c;
+  const int64_t tr = tile / tiles_c, tc = tile - (tile / tiles_c) * tiles_c;
   const int64_t r0 = tr * kTile, c0 = tc * kTile;
   const int rg = t >> 4, cc = t & 15;
   float scale;
@@ -113,7 +117,7 @@ __global__ __launch_bounds__(kThreads) void cast_kernel(const uint16_t* __restri
       sat_above = e <= 254 ? (((uint32_t)e << 7) | 0x60u) : 0x7F7Fu;
     }
     nonfinite = (flags & FP8_FLAG_NONFINITE) != 0u;
-    if (blockIdx.x == 0 && t == 0) {
+    if (tile == 0 && t == 0) {
       union { uint32_t u; float f; } a;
       a.u = mag << 16;
       s->amax = a.f;
@@ -175,7 +179,7 @@ __global__ __launch_bounds__(kThreads) void cast_kernel(const uint16_t* __restri
     // block sum, one atomic per block that saw a saturation
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) nsat += (uint32_t)__shfl_xor((int)nsat, off, 64);
-    __shared__ uint32_t wsum[kThreads / 64];
+    uint32_t* const wsum = g_wsum;
     if ((t & 63) == 0) wsum[t >> 6] = nsat;
     __syncthreads();
     if (t == 0) {
@@ -212,6 +216,48 @@ __global__ __launch_bounds__(kThreads) void cast_kernel(const uint16_t* __restri
   }
 }
 
+template <int FMT, bool DERIVE, bool COUNT = false>
+__global__ __launch_bounds__(kThreads) void cast_kernel(const uint16_t* __restrict__ x, int64_t rows,
+                                                        int64_t cols, int64_t tiles_c, fp8_scale_t* s,
+                                                        uint8_t* __restrict__ out_row,
+                                                        uint8_t* __restrict__ out_t, int margin,
+                                                        int mu_log2) {
+  cast_tile<FMT, DERIVE, COUNT>(x, rows, cols, tiles_c, s, out_row, out_t, margin, mu_log2, (int64_t)blockIdx.x);
+}
+
+// Derive-casts of up to kQuantBatchMax tensors in one launch: blocks
+// first_block[i] .. first_block[i+1]-1 take tensor i's tiles (an empty
+// tensor gets one block, which publishes its record). Each block does what
+// fp8_quantize's cast block for that tile does.
+struct CastEntry {
+  const uint16_t* x;
+  int64_t rows, cols, tiles_c;
+  fp8_scale_t* s;
+  uint8_t* out_row;
+  uint8_t* out_t;
+  int fmt, margin, mu_log2, first_block;
+};
+struct CastBatch {
+  CastEntry e[kQuantBatchMax];
+  int count;
+};
+
+__global__ __launch_bounds__(kThreads) void cast_batch_kernel(CastBatch b) {
+  const int blk = (int)blockIdx.x;
+  int i = 0;
+#pragma unroll
+  for (int k = 1; k < kQuantBatchMax; ++k)
+    if (k < b.count && blk >= b.e[k].first_block) i = k;
+  const CastEntry& e = b.e[i];
+  const int64_t tile = blk - e.first_block;
+  if (e.fmt == FP8_E4M3)
+    cast_tile<FP8_E4M3, true, false>(e.x, e.rows, e.cols, e.tiles_c, e.s, e.out_row, e.out_t, e.margin, e.mu_log2,
+                                     tile);
+  else
+    cast_tile<FP8_E5M2, true, false>(e.x, e.rows, e.cols, e.tiles_c, e.s, e.out_row, e.out_t, e.margin, e.mu_log2,
+                                     tile);
+}
+
 template <bool DERIVE, bool COUNT = false>
 hipError_t launch_cast_t(const void* x, int64_t rows, int64_t cols, int fmt, fp8_scale_t* s,
                          uint8_t* out_row, uint8_t* out_t, int margin, int mu_log2, hipStream_t st) {
@@ -244,6 +290,34 @@ hipError_t launch_quantize(const void* x, int64_t rows, int64_t cols, int fmt, i
     return launch_cast_t<true>(x, 0, 0, fmt, s, nullptr, nullptr, margin, mu_log2, st);
   }
   return launch_cast_t<true>(x, rows, cols, fmt, s, out_row, out_t, margin, mu_log2, st);
+}
+
+hipError_t launch_quantize_batch(const QuantDesc* d, int count, hipStream_t st) {
+  if (count < 1 || count > kQuantBatchMax) return hipErrorInvalidValue;
+  hipError_t e = launch_amax_batch(d, count, st);
+  if (e != hipSuccess) return e;
+  CastBatch b{};
+  b.count = count;
+  int blocks = 0;
+  for (int i = 0; i < count; ++i) {
+    CastEntry& c = b.e[i];
+    const bool empty = d[i].rows == 0 || d[i].cols == 0 || (!d[i].out_row && !d[i].out_t);
+    c.x = (const uint16_t*)d[i].x;
+    c.rows = empty ? 0 : d[i].rows;
+    c.cols = empty ? 0 : d[i].cols;
+    c.tiles_c = empty ? 1 : (d[i].cols + kTile - 1) / kTile;
+    c.s = d[i].s;
+    c.out_row = empty ? nullptr : d[i].out_row;
+    c.out_t = empty ? nullptr : d[i].out_t;
+    c.fmt = d[i].fmt;
+    c.margin = d[i].margin;
+    c.mu_log2 = d[i].mu_log2;
+    c.first_block = blocks;
+    // an empty tensor: one block that reads nothing and publishes the record
+    blocks += empty ? 1 : (int)(((d[i].rows + kTile - 1) / kTile) * c.tiles_c);
+  }
+  hipLaunchKernelGGL(cast_batch_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, st, b);
+  return hipGetLastError();
 }
 
 hipError_t launch_wgrad_cast(const void* dw, int64_t rows, int64_t cols, fp8_scale_t* s, uint8_t* out_row,

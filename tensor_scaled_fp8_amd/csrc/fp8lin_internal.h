@@ -113,6 +113,20 @@ hipError_t launch_amax_gen(const void* x, int64_t n, fp8_scale_t* s, hipStream_t
 // amax pass + cast that derives the scale (fp8_quantize)
 hipError_t launch_quantize(const void* x, int64_t rows, int64_t cols, int fmt, int margin, int mu_log2,
                            fp8_scale_t* s, uint8_t* out_row, uint8_t* out_t, hipStream_t st);
+// Several tensors quantised in two launches (fp8_quantize_batch).
+constexpr int kQuantBatchMax = 4;
+struct QuantDesc {
+  const void* x;
+  int64_t rows, cols;
+  int fmt, margin, mu_log2;
+  fp8_scale_t* s;
+  uint8_t* out_row;
+  uint8_t* out_t;
+};
+// the amax passes of count tensors (1..kQuantBatchMax, distinct records) in one launch
+hipError_t launch_amax_batch(const QuantDesc* d, int count, hipStream_t st);
+// amax passes, then the derive-casts, each tensor as launch_quantize would do it
+hipError_t launch_quantize_batch(const QuantDesc* d, int count, hipStream_t st);
 // ta / tb: operand stored reduction-major (A [R, M], B [R, N]) instead of
 // one row per output index (A [M, R], B [N, R])
 hipError_t launch_gemm(const uint8_t* A, int fa, bool ta, const fp8_scale_t* sa, const uint8_t* B, int fb, bool tb,

@@ -31,7 +31,7 @@ def test_header_functions_all_exported():
     for n in names:
         assert hasattr(lib, n), n
         assert n in _lib.SIGNATURES, f"binding lacks {n}"
-    assert lib.fp8_abi_version() == 7
+    assert lib.fp8_abi_version() == 8
 
 
 def test_status_strings():
@@ -116,6 +116,24 @@ def test_argument_validation_without_launch():
     assert gp(ctypes.byref(good), ctypes.byref(misaligned), None) == INV
     no_rec = _lib.GemmArgs(ok, 0, 1, None, ok, 1, 1, ok, 16, 16, 16, ok)
     assert gp(ctypes.byref(no_rec), ctypes.byref(good), None) == INV
+    # quantize batch: 1..4 argument sets, each checked as fp8_quantize's, distinct records
+    qb = lib.fp8_quantize_batch
+    QA = _lib.QuantizeArgs
+    one = (QA * 1)(QA(ok, 16, 16, 0, 0, 0, ok, ok, None))
+    assert qb(None, 1, None) == INV
+    assert qb(one, 0, None) == INV
+    five = (QA * 5)(*[QA(ok, 16, 16, 0, 0, 0, ok + 64 * i, ok, None) for i in range(5)])
+    assert qb(five, 5, None) == INV
+    dup = (QA * 2)(QA(ok, 16, 16, 0, 0, 0, ok, ok, None), QA(ok, 16, 16, 1, 0, 0, ok, ok, None))
+    assert qb(dup, 2, None) == INV
+    bad = (QA * 2)(QA(ok, 16, 16, 0, 0, 0, ok, ok, None), QA(ok, 16, 24, 1, 0, 0, ok + 64, ok, None))
+    assert qb(bad, 2, None) == UNS
+    bad = (QA * 2)(QA(ok, 16, 16, 0, 0, 0, ok, ok, None), QA(ok, 16, 16, 2, 0, 0, ok + 64, ok, None))
+    assert qb(bad, 2, None) == INV
+    bad = (QA * 2)(QA(ok, 16, 16, 0, 0, 0, ok, ok, None), QA(ok, 16, 16, 1, 0, 0, ok + 64, ok + 3, None))
+    assert qb(bad, 2, None) == INV
+    bad = (QA * 1)(QA(ok, 16, 16, 0, 5000, 0, ok, ok, None))
+    assert qb(bad, 1, None) == INV
     # linear: workspace checks
     ws = _lib.LinearWs(ok, ok, ok, ok, ok, ok, ok, ok, ok)
     assert lib.fp8_linear_fwd(_vp(ok), _vp(ok), 16, 16, 16, 0, None, _vp(ok), None) == INV
