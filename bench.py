@@ -7,7 +7,8 @@ layer, 4096 tokens, hidden 4096: qkv 4096->12288, proj 4096->4096,
 up 4096->16384, down 16384->4096):
     quantize(X), quantize(W)   amax + scale + cast to row-major FP8 (E4M3),
                                both tensors in one launch pair (fp8_quantize_batch)
-    Y  = FP8 GEMM (x8, w8 read reduction-major)
+    Y  = FP8 GEMM (x8, w8 read reduction-major; a last wave at most half
+         full is split into reduction halves over the workspace)
     quantize(dY)               (E5M2)
     dX = FP8 GEMM (dy8, w8) and dW = FP8 GEMM (x8, dy8 both read
     reduction-major), both in one launch (fp8_gemm_pair)
@@ -116,7 +117,8 @@ def main():
                      dict(x=d["X"], fmt="e4m3", s=ws.sx, margin=margin, out_row=ws.x8, transposed=False),
                      dict(x=d["W"], fmt="e4m3", s=ws.sw, margin=margin, out_row=ws.w8, transposed=False)])),
                 ("gemm", f"{n}.fwd {L.M}x{L.N}x{L.K}", 0, 2 * L.M * L.N * L.K,
-                 lambda: tsf.fp8_gemm(ws.x8, "e4m3", ws.sx, ws.w8, "e4m3", ws.sw, d["Y"], "rows", "cols")),
+                 lambda: tsf.fp8_gemm(ws.x8, "e4m3", ws.sx, ws.w8, "e4m3", ws.sw, d["Y"], "rows", "cols",
+                                      workspace=ws.scratch)),
                 ("quant", f"{n}.dY", 5 * L.M * L.N, 0,
                  lambda: tsf.fp8_quantize(d["dY"], "e5m2", ws.sdy, margin, mu, ws.dy8, transposed=False)),
                 ("gemm", f"{n}.bwd dgrad {L.M}x{L.K}x{L.N} + wgrad {L.K}x{L.N}x{L.M}", 0, 4 * L.M * L.K * L.N,

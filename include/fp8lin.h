@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define FP8LIN_ABI_VERSION 8
+#define FP8LIN_ABI_VERSION 9
 
 typedef enum fp8_fmt {
   FP8_E4M3 = 0, /* OCP E4M3FN: weights and activations [AMAX bullet 4] */
@@ -263,6 +263,44 @@ fp8_status fp8_gemm(const uint8_t* A, fp8_fmt fa, fp8_layout la, const fp8_scale
                     fp8_fmt fb, fp8_layout lb, const fp8_scale_t* sb, int64_t M, int64_t N, int64_t R,
                     void* C_bf16, hipStream_t stream);
 
+/* When fp8_gemm_ws splits the last wave of a GEMM. */
+typedef enum {
+  FP8_SPLIT_AUTO = 0,  /* when it pays: the conditions below and R >= 16384 */
+  FP8_SPLIT_NEVER = 1,
+  FP8_SPLIT_TAIL = 2   /* whenever the conditions below hold (R >= 512) */
+} fp8_split;
+
+/*
+ * Workspace bytes fp8_gemm_ws uses for this GEMM on the current device
+ * with this split mode: 0 when it would not split. Only E4M3 x E4M3 GEMMs
+ * (the forward) with R a multiple of 256 split: when the output tiles
+ * (256 x 256) leave a last wave at most half full on the device's CUs,
+ * each tile of that wave is computed as two reduction halves (FP32
+ * partial sums, 512 KiB per tile) that a second kernel adds, so the last
+ * wave runs twice as many blocks of half the length. The fixup launch and
+ * the partials' traffic outweigh the saving for short reductions
+ * (measured on the GPT-13B/175B-style forward GEMMs: R = 5120-12288
+ * 4-9 % slower, R = 20480 3 % and R = 49152 12 % faster), hence the
+ * AUTO threshold. Negative sizes give 0.
+ */
+size_t fp8_gemm_workspace_bytes(fp8_fmt fa, fp8_fmt fb, int64_t M, int64_t N, int64_t R, fp8_split split);
+
+/*
+ * fp8_gemm with a caller workspace (same arguments, checks and result
+ * bound): when fp8_gemm_workspace_bytes (same split mode) is nonzero and
+ * workspace_bytes covers it, the last partial wave's tiles are split as
+ * described there (two launches: the GEMM and the fixup), else this is
+ * fp8_gemm. split outside fp8_split -> FP8_ERR_INVALID. A split
+ * tile's sum is half0 + half1 in FP32, so it may differ from fp8_gemm's
+ * result by accumulation order (inside the GEMM tolerance); the result is
+ * deterministic. workspace: device, 16-B aligned, or NULL (no split); not
+ * read before it is written; concurrent calls must not share it.
+ */
+fp8_status fp8_gemm_ws(const uint8_t* A, fp8_fmt fa, fp8_layout la, const fp8_scale_t* sa, const uint8_t* B,
+                       fp8_fmt fb, fp8_layout lb, const fp8_scale_t* sb, int64_t M, int64_t N, int64_t R,
+                       void* C_bf16, fp8_split split, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream);
+
 /* The arguments of one fp8_gemm call. */
 typedef struct fp8_gemm_args {
   const uint8_t* A;
@@ -301,6 +339,8 @@ fp8_status fp8_gemm_pair(const fp8_gemm_args* first, const fp8_gemm_args* second
  *   where needed, see fp8_gemm); a transposed copy is written when its
  *   pointer is set, for callers that want it.
  *   sx, sw, sdy: zero-initialised scaling records (see fp8_scale_t).
+ *   scratch, scratch_bytes: optional workspace of the forward GEMM
+ *   (16-B aligned, or NULL; fp8_linear_scratch_bytes tells the size).
  * The forward fills x8, w8, sx, sw (and x8t, w8t if set); the backward
  * reads them and fills dy8, sdy (and dy8t if set).
  */
@@ -314,7 +354,13 @@ typedef struct fp8_linear_ws {
   fp8_scale_t* sx;
   fp8_scale_t* sw;
   fp8_scale_t* sdy;
+  void* scratch;          /* forward GEMM workspace (fp8_gemm_ws), or NULL */
+  size_t scratch_bytes;
 } fp8_linear_ws;
+
+/* Scratch bytes that let fp8_linear_fwd split its GEMM's last wave
+ * (fp8_gemm_workspace_bytes with FP8_SPLIT_AUTO); 0 when it would not. */
+size_t fp8_linear_scratch_bytes(int64_t M, int64_t K, int64_t N);
 
 /*
  * Forward of one linear, Y = X W: fp8_quantize of X and W (E4M3), then the

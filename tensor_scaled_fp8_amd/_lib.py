@@ -29,6 +29,10 @@ SIGNATURES = {
     "fp8_gemm_nt": (c_int, [c_vp, c_int, c_vp, c_vp, c_int, c_vp, c_i64, c_i64, c_i64, c_vp, c_vp]),
     "fp8_gemm": (c_int, [c_vp, c_int, c_int, c_vp, c_vp, c_int, c_int, c_vp, c_i64, c_i64, c_i64, c_vp, c_vp]),
     "fp8_gemm_pair": (c_int, [c_vp, c_vp, c_vp]),
+    "fp8_gemm_ws": (c_int, [c_vp, c_int, c_int, c_vp, c_vp, c_int, c_int, c_vp, c_i64, c_i64, c_i64, c_vp, c_int,
+                            c_vp, ctypes.c_size_t, c_vp]),
+    "fp8_gemm_workspace_bytes": (ctypes.c_size_t, [c_int, c_int, c_i64, c_i64, c_i64, c_int]),
+    "fp8_linear_scratch_bytes": (ctypes.c_size_t, [c_i64, c_i64, c_i64]),
     "fp8_linear_fwd": (c_int, [c_vp, c_vp, c_i64, c_i64, c_i64, c_int, c_vp, c_vp, c_vp]),
     "fp8_linear_bwd": (c_int, [c_vp, c_i64, c_i64, c_i64, c_int, c_int, c_vp, c_vp, c_vp, c_vp]),
     "fp8_linear_fwd_cached": (c_int, [c_vp, c_i64, c_i64, c_i64, c_int, c_int, c_vp, c_vp, c_vp, c_vp, c_vp,
@@ -45,13 +49,15 @@ FP8_OPERAND_ROWS, FP8_OPERAND_COLS = 0, 1
 FP8_OK, FP8_ERR_INVALID, FP8_ERR_UNSUPPORTED, FP8_ERR_HIP = 0, 1, 2, 3
 FLAG_NONFINITE, FLAG_ZERO, FLAG_CLAMPED = 1, 2, 4
 FP8_SCALING_AMAX, FP8_SCALING_FIXED = 0, 1
-ABI_VERSION = 8
+FP8_SPLIT_AUTO, FP8_SPLIT_NEVER, FP8_SPLIT_TAIL = 0, 1, 2
+ABI_VERSION = 9
 
 
 class LinearWs(ctypes.Structure):
     """fp8_linear_ws: host struct of device pointers."""
     _fields_ = [("x8", c_vp), ("x8t", c_vp), ("w8", c_vp), ("w8t", c_vp), ("dy8", c_vp),
-                ("dy8t", c_vp), ("sx", c_vp), ("sw", c_vp), ("sdy", c_vp)]
+                ("dy8t", c_vp), ("sx", c_vp), ("sw", c_vp), ("sdy", c_vp), ("scratch", c_vp),
+                ("scratch_bytes", ctypes.c_size_t)]
 
 
 class QuantizeArgs(ctypes.Structure):

@@ -17,6 +17,7 @@ import torch
 
 from . import _lib
 from ._lib import (FP8_E4M3, FP8_E5M2, FP8_OPERAND_COLS, FP8_OPERAND_ROWS, FP8_SCALING_AMAX, FP8_SCALING_FIXED,
+                   FP8_SPLIT_AUTO, FP8_SPLIT_NEVER, FP8_SPLIT_TAIL,
                    GemmArgs, LinearWs, QuantizeArgs, check, load)
 
 SCALE_WORDS = 16         # sizeof(fp8_scale_t) / 4
@@ -200,12 +201,31 @@ def _gemm_args(a: torch.Tensor, fa, sa: torch.Tensor, b: torch.Tensor, fb, sb: t
 
 
 def fp8_gemm(a: torch.Tensor, fa, sa: torch.Tensor, b: torch.Tensor, fb, sb: torch.Tensor,
-             out: Optional[torch.Tensor] = None, a_layout: str = "rows", b_layout: str = "rows") -> torch.Tensor:
+             out: Optional[torch.Tensor] = None, a_layout: str = "rows", b_layout: str = "rows",
+             workspace: Optional[torch.Tensor] = None, split: str = "auto") -> torch.Tensor:
     """C[M, N] (bf16) = 2^-(bias_a + bias_b) * sum_r A(i, r) B(j, r) on FP8 codes,
-    each operand either "rows" (A [M, R], B [N, R]) or "cols" (A [R, M], B [R, N])."""
+    each operand either "rows" (A [M, R], B [N, R]) or "cols" (A [R, M], B [R, N]).
+    With a workspace (uint8 device tensor, see gemm_workspace_bytes) the
+    last partial wave of an E4M3 x E4M3 GEMM may be split (fp8_gemm_ws;
+    split "auto", "never" or "tail")."""
     g, out = _gemm_args(a, fa, sa, b, fb, sb, out, a_layout, b_layout)
-    check(load().fp8_gemm(g.A, g.fa, g.la, g.sa, g.B, g.fb, g.lb, g.sb, g.M, g.N, g.R, g.C, _stream(a)), "fp8_gemm")
+    if workspace is None:
+        check(load().fp8_gemm(g.A, g.fa, g.la, g.sa, g.B, g.fb, g.lb, g.sb, g.M, g.N, g.R, g.C, _stream(a)),
+              "fp8_gemm")
+    else:
+        check(load().fp8_gemm_ws(g.A, g.fa, g.la, g.sa, g.B, g.fb, g.lb, g.sb, g.M, g.N, g.R, g.C, SPLITS[split],
+                                 _dev(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(a)),
+              "fp8_gemm_ws")
     return out
+
+
+SPLITS = {"auto": FP8_SPLIT_AUTO, "never": FP8_SPLIT_NEVER, "tail": FP8_SPLIT_TAIL}
+
+
+def gemm_workspace_bytes(fa, fb, M: int, N: int, R: int, split: str = "auto") -> int:
+    """Workspace bytes fp8_gemm(..., workspace=, split=) uses for this GEMM
+    on the current device (0: it would not split)."""
+    return int(load().fp8_gemm_workspace_bytes(_fmt(fa), _fmt(fb), M, N, R, SPLITS[split]))
 
 
 def fp8_gemm_pair(first: dict, second: dict):
@@ -226,7 +246,8 @@ class LinearWorkspace:
     """Device buffers of one FP8 linear: the row-major FP8 copies of X, W
     and dY, the three scaling records and, with transposed=True, the
     transposed FP8 copies as well (the linear entry points then also write
-    them; their GEMMs never need them)."""
+    them; their GEMMs never need them), and the forward GEMM's workspace
+    when its shape splits the last wave."""
 
     def __init__(self, M: int, K: int, N: int, device="cuda", transposed: bool = False):
         u8 = dict(dtype=torch.uint8, device=device)
@@ -239,9 +260,12 @@ class LinearWorkspace:
         self.dy8t = torch.empty((N, M), **u8) if transposed else None
         self.scales = new_scale(3, device)
         self.sx, self.sw, self.sdy = self.scales[0], self.scales[1], self.scales[2]
+        # forward GEMM workspace (last-wave split), when this shape uses one
+        nb = int(load().fp8_linear_scratch_bytes(M, K, N)) if torch.device(device).type == "cuda" else 0
+        self.scratch = torch.empty(nb, **u8) if nb else None
         self.c = LinearWs(*[None if t is None else t.data_ptr()
                             for t in (self.x8, self.x8t, self.w8, self.w8t, self.dy8, self.dy8t, self.sx,
-                                      self.sw, self.sdy)])
+                                      self.sw, self.sdy, self.scratch)], nb)
 
 
 def fp8_linear_fwd(X: torch.Tensor, W: torch.Tensor, ws: LinearWorkspace, margin: int = 0,

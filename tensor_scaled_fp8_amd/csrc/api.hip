@@ -156,6 +156,22 @@ fp8_status fp8_gemm(const uint8_t* A, fp8_fmt fa, fp8_layout la, const fp8_scale
                                 C_bf16, stream));
 }
 
+size_t fp8_gemm_workspace_bytes(fp8_fmt fa, fp8_fmt fb, int64_t M, int64_t N, int64_t R, fp8_split split) {
+  if (M < 0 || N < 0 || R < 0) return 0;
+  return gemm_tail_split((int)fa, (int)fb, M, N, R, (int)split).bytes;
+}
+
+fp8_status fp8_gemm_ws(const uint8_t* A, fp8_fmt fa, fp8_layout la, const fp8_scale_t* sa, const uint8_t* B,
+                       fp8_fmt fb, fp8_layout lb, const fp8_scale_t* sb, int64_t M, int64_t N, int64_t R,
+                       void* C_bf16, fp8_split split, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const fp8_status st = check_gemm(A, fa, la, sa, B, fb, lb, sb, M, N, R, C_bf16);
+  if (st != FP8_OK) return st;
+  if (split != FP8_SPLIT_AUTO && split != FP8_SPLIT_NEVER && split != FP8_SPLIT_TAIL) return FP8_ERR_INVALID;
+  if (workspace && !aligned16(workspace)) return FP8_ERR_INVALID;
+  return hip_status(launch_gemm_ws(A, fa, la == FP8_OPERAND_COLS, sa, B, fb, lb == FP8_OPERAND_COLS, sb, M, N, R,
+                                   C_bf16, (int)split, workspace, workspace_bytes, stream));
+}
+
 fp8_status fp8_gemm_pair(const fp8_gemm_args* first, const fp8_gemm_args* second, hipStream_t stream) {
   if (!first || !second) return FP8_ERR_INVALID;
   GemmDesc g[2];
@@ -184,7 +200,7 @@ static fp8_status check_ws(const fp8_linear_ws* ws, bool fwd) {
                      fwd ? (const void*)ws->x8 : (const void*)ws->sdy};
   for (const void* q : p)
     if (!q || !aligned16(q)) return FP8_ERR_INVALID;
-  const void* o[] = {ws->x8t, ws->w8t, ws->dy8t};
+  const void* o[] = {ws->x8t, ws->w8t, ws->dy8t, ws->scratch};
   for (const void* q : o)
     if (q && !aligned16(q)) return FP8_ERR_INVALID;
   return FP8_OK;
@@ -206,8 +222,15 @@ fp8_status fp8_linear_fwd(const void* X, const void* W, int64_t M, int64_t K, in
   const QuantDesc q[2] = {QuantDesc{X, M, K, FP8_E4M3, margin, 0, ws->sx, ws->x8, ws->x8t},
                           QuantDesc{W, K, N, FP8_E4M3, margin, 0, ws->sw, ws->w8, ws->w8t}};
   if (launch_quantize_batch(q, 2, stream) != hipSuccess) return FP8_ERR_HIP;
-  // Y[m, n] = sum_k x8[m, k] w8[k, n]: w8 read reduction-major
-  return hip_status(launch_gemm(ws->x8, FP8_E4M3, false, ws->sx, ws->w8, FP8_E4M3, true, ws->sw, M, N, K, Y, stream));
+  // Y[m, n] = sum_k x8[m, k] w8[k, n]: w8 read reduction-major (last wave
+  // split over the scratch workspace when it is given and large enough)
+  return hip_status(launch_gemm_ws(ws->x8, FP8_E4M3, false, ws->sx, ws->w8, FP8_E4M3, true, ws->sw, M, N, K, Y,
+                                   FP8_SPLIT_AUTO, ws->scratch, ws->scratch_bytes, stream));
+}
+
+size_t fp8_linear_scratch_bytes(int64_t M, int64_t K, int64_t N) {
+  if (M < 0 || K < 0 || N < 0) return 0;
+  return gemm_tail_split(FP8_E4M3, FP8_E4M3, M, N, K, FP8_SPLIT_AUTO).bytes;
 }
 
 fp8_status fp8_linear_bwd(const void* dY, int64_t M, int64_t K, int64_t N, int margin, int mu_log2,

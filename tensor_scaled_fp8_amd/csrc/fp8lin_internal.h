@@ -132,6 +132,25 @@ hipError_t launch_quantize_batch(const QuantDesc* d, int count, hipStream_t st);
 hipError_t launch_gemm(const uint8_t* A, int fa, bool ta, const fp8_scale_t* sa, const uint8_t* B, int fb, bool tb,
                        const fp8_scale_t* sb, int64_t M, int64_t N, int64_t R, void* C,
                        hipStream_t st);
+// Tail split of a forward-format GEMM (E4M3 x E4M3, R a multiple of 256):
+// when the tiles leave a last wave at most half full, those ntail tiles
+// are computed in two reduction halves each (FP32 partials in a caller
+// workspace of `bytes`) and summed by a fixup kernel, after the nfull
+// tiles of the whole waves. mode: FP8_SPLIT_AUTO also needs R >= 16384
+// (the fixup launch and the partials' traffic cost more than half a
+// shorter tile), FP8_SPLIT_TAIL only R >= 512, FP8_SPLIT_NEVER never.
+// ntail = 0: no split for this shape on the current device.
+struct TailSplit {
+  int nfull, ntail;
+  size_t bytes;
+};
+constexpr int64_t kSplitMinR = 16384;
+TailSplit gemm_tail_split(int fa, int fb, int64_t M, int64_t N, int64_t R, int mode);
+// launch_gemm, with the tail split when gemm_tail_split plans one and the
+// workspace holds its partials (else exactly launch_gemm)
+hipError_t launch_gemm_ws(const uint8_t* A, int fa, bool ta, const fp8_scale_t* sa, const uint8_t* B, int fb,
+                          bool tb, const fp8_scale_t* sb, int64_t M, int64_t N, int64_t R, void* C, int mode,
+                          void* ws, size_t ws_bytes, hipStream_t st);
 // One GEMM of a pair (the arguments of launch_gemm).
 struct GemmDesc {
   const uint8_t* A;

@@ -62,6 +62,7 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v2i __attribute__((ext_vector_type(2)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
@@ -149,9 +150,31 @@ __shared__ uint4 g_slot1[kStageBytes / 16];
 // reduction bytes contiguous (A [M, R], B [N, R]); true: reduction-major
 // (A [R, M], B [R, N]), staged in LDS as [k][output] and turned into MFMA
 // fragments by transposing LDS reads.
+// Tile order: workgroups are dealt round-robin to the 8 XCDs, so index
+// pid runs on XCD pid % 8; each XCD gets one contiguous range of tiles
+// (when the count is a multiple of 8), rastered in groups of kGroupM tile
+// rows so that an XCD's concurrent tiles share operand panels in its L2.
+__device__ inline void tile_origin(int pid, int tiles_m, int tiles_n, int& m0, int& n0) {
+  const int nblocks = tiles_m * tiles_n;
+  if ((nblocks & 7) == 0) pid = (pid & 7) * (nblocks >> 3) + (pid >> 3);
+  const int per_group = kGroupM * tiles_n;
+  const int group = pid / per_group;
+  const int first_m = group * kGroupM;
+  const int gsize = min(tiles_m - first_m, kGroupM);
+  const int in_group = pid - group * per_group;
+  m0 = (first_m + in_group % gsize) * kBM;
+  n0 = (in_group / gsize) * kBN;
+}
+
 // tile: index of the output tile within the problem's tile grid.
-template <int FA, int FB, bool AMAX, bool TA, bool TB>
-__device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, fp8_scale_t* s_out) {
+// HALF: the block takes reduction half `half` of the tile (stages
+// [half * nk / 2, (half + 1) * nk / 2), R a multiple of 256) and, instead
+// of the epilogue, stores its unscaled FP32 sums to `part` (65536 floats,
+// in register order: float4 r4 = (mi * 4 + ni) * 4 + q of thread t at
+// float offset 1024 r4 + 4 t); gemm_tail_fixup_kernel adds the two halves.
+template <int FA, int FB, bool AMAX, bool TA, bool TB, bool HALF = false>
+__device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, fp8_scale_t* s_out, int half = 0,
+                                          float* part = nullptr) {
   const uint8_t* __restrict__ A = p.A;
   const uint8_t* __restrict__ B = p.B;
   const fp8_scale_t* __restrict__ sa = p.sa;
@@ -166,17 +189,8 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, fp8_sca
   using S1 = std::integral_constant<int, 1>;
 
   // ---- tile selection: XCD-contiguous ranges, grouped raster inside ----
-  const int nblocks = tiles_m * tiles_n;
-  int pid = tile;
-  if ((nblocks & 7) == 0) pid = (pid & 7) * (nblocks >> 3) + (pid >> 3);
-  const int per_group = kGroupM * tiles_n;
-  const int group = pid / per_group;
-  const int first_m = group * kGroupM;
-  const int gsize = min(tiles_m - first_m, kGroupM);
-  const int in_group = pid - group * per_group;
-  const int tm = first_m + in_group % gsize;
-  const int tn = in_group / gsize;
-  const int m0 = tm * kBM, n0 = tn * kBN;
+  int m0, n0;
+  tile_origin(tile, tiles_m, tiles_n, m0, n0);
 
   const int t = threadIdx.x, lane = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);  // wave index, scalar
@@ -219,8 +233,11 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, fp8_sca
     offa[i] = pa + ca;
     offb[i] = pb + cb;
   }
-  const int nk = (R + kBK - 1) / kBK;      // stages
-  const int nfull = R / kBK;               // full stages (all but a partial last one)
+  // stages of this block: all, or one half (HALF: R is a multiple of 256,
+  // so both halves are whole stages); s0 = the first one
+  const int s0 = HALF ? half * (R / (2 * kBK)) : 0;
+  const int nk = HALF ? R / (2 * kBK) : (R + kBK - 1) / kBK;
+  const int nfull = HALF ? nk : R / kBK;   // full stages (all but a partial last one)
 
   // Buffer resources (base + byte count of each operand): being buffer (not
   // flat) loads, they leave the compiler's count of outstanding LDS reads
@@ -232,8 +249,8 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, fp8_sca
   // the 16 loads (8 of A, 8 of B) of one full stage
   auto issue_full = [&](lds_u8* sl, int stage) {
     // wave-uniform; below 2^32 (operands are below 4 GiB), passed as int
-    const int koffa = (int)((uint32_t)stage * kBK * (TA ? (uint32_t)M : 1u));
-    const int koffb = (int)((uint32_t)stage * kBK * (TB ? (uint32_t)N : 1u));
+    const int koffa = (int)((uint32_t)(s0 + stage) * kBK * (TA ? (uint32_t)M : 1u));
+    const int koffb = (int)((uint32_t)(s0 + stage) * kBK * (TB ? (uint32_t)N : 1u));
     lds_u8* sa_ = sl + (8 * w) * 1024;
     lds_u8* sb_ = sl + kOpBytes + (8 * w) * 1024;
 #pragma unroll
@@ -248,7 +265,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, fp8_sca
       issue_full(sl, stage);
       return;
     }
-    const int k0 = stage * kBK;
+    const int k0 = (s0 + stage) * kBK;
     lds_u8* sa_ = sl + (8 * w) * 1024;
     lds_u8* sb_ = sl + kOpBytes + (8 * w) * 1024;
     // first k of lane's 16 bytes (row layout) or lane's k-row (reduction-major)
@@ -456,6 +473,26 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, fp8_sca
   wait_vmcnt<0>();
   block_sync_lds();
 
+  if constexpr (HALF) {
+    // partial sums out, 4 KB contiguous per store instruction (the thread
+    // index through an empty asm keeps the addressing out of the k-loop)
+    int te = t;
+    asm volatile("" : "+v"(te));
+    float* dst = part + 4 * te;
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni) {
+        const v16f a = acc[mi][ni];
+        float* d = dst + 4096 * (mi * 4 + ni);
+        *(f32x4*)(d + 0) = __builtin_shufflevector(a, a, 0, 1, 2, 3);
+        *(f32x4*)(d + 1024) = __builtin_shufflevector(a, a, 4, 5, 6, 7);
+        *(f32x4*)(d + 2048) = __builtin_shufflevector(a, a, 8, 9, 10, 11);
+        *(f32x4*)(d + 3072) = __builtin_shufflevector(a, a, 12, 13, 14, 15);
+      }
+    return;
+  }
+
   // ---- epilogue: 2^s (exact power-of-two scaling), bf16 RNE, then the
   // 256 x 256 bf16 tile (128 KB: 64 rows of 512 bytes per half buffer) is
   // staged row-major in LDS so the block writes C in whole 512-byte rows of
@@ -570,6 +607,80 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pair_kernel(GemmParams p0, G
   else gemm_tile<FA1, FB1, false, TA1, TB1>(p1, b - n0, nullptr);
 }
 
+// Tail split: tiles [0, nfull) as in gemm_nt_kernel; each of the ntail
+// tiles after them (the last, partial wave: ntail <= half the CUs) is
+// taken by two blocks, one per reduction half, which store FP32 partial
+// sums to part (two 65536-float slots per tail tile). The last wave then
+// runs 2 * ntail half-length blocks instead of ntail whole ones.
+template <int FA, int FB, bool TA, bool TB>
+__global__ __launch_bounds__(kThreads, 1) void gemm_tailsplit_kernel(GemmParams p, int nfull, float* part) {
+  const int b = (int)blockIdx.x;
+  if (b < nfull) {
+    gemm_tile<FA, FB, false, TA, TB>(p, b, nullptr);
+  } else {
+    const int u = b - nfull, j = u >> 1;
+    gemm_tile<FA, FB, false, TA, TB, true>(p, nfull + j, nullptr, u & 1, part + (size_t)(2 * j + (u & 1)) * 65536);
+  }
+}
+
+// C tiles of the tail: half 0 + half 1 (in that order, FP32), times
+// 2^-(ba + bb), bf16 RNE; staged in LDS and written in whole rows as the
+// GEMM epilogue does. Block j finishes tail tile nfull + j.
+__global__ __launch_bounds__(kThreads, 1) void gemm_tail_fixup_kernel(GemmParams p, int nfull, const float* part) {
+  const int j = (int)blockIdx.x;
+  const int t = threadIdx.x, lane = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6), wm = w >> 1, wn = w & 1;
+  const int frow = lane & 31, g = lane >> 5;
+  int m0, n0;
+  tile_origin(nfull + j, p.tiles_m, p.tiles_n, m0, n0);
+  const int M = p.M, N = p.N;
+  const int shift = -(p.sa->bias + p.sb->bias);
+  const float* h0 = part + (size_t)(2 * j) * 65536 + 4 * t;
+  const float* h1 = h0 + 65536;
+  lds_u8* const lds0 = (lds_u8*)g_slot0;
+  lds_u8* const lds1 = (lds_u8*)g_slot1;
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi) {
+    const int row = 128 * wm + 32 * mi + frow;
+    lds_u8* crow = (wm ? lds1 : lds0) + (mi >> 1) * (kStageBytes / 2) + (row & 63) * 512;
+    f32x4 a[16], b[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      a[k] = __builtin_nontemporal_load((const f32x4*)(h0 + 1024 * (mi * 16 + k)));
+      b[k] = __builtin_nontemporal_load((const f32x4*)(h1 + 1024 * (mi * 16 + k)));
+    }
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 sum = a[ni * 4 + q] + b[ni * 4 + q];  // half 0 + half 1
+        const f32x2 lo = {ldexpf(sum.x, shift), ldexpf(sum.y, shift)};
+        const f32x2 hi = {ldexpf(sum.z, shift), ldexpf(sum.w, shift)};
+        const uint32_t p0 = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2));
+        const uint32_t p1 = __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2));
+        const int chunk = 16 * wn + 4 * ni + q;
+        *(lds_u32x2*)(crow + ((chunk ^ (row & 31)) << 4) + 8 * g) = (u32x2){p0, p1};
+      }
+    }
+  }
+  __syncthreads();
+  // drain as the GEMM epilogue: lane t takes 16-byte chunk c = t % 32 of
+  // rows r0 + 8k (r0 = t / 32) of each 64-row region
+  const int c = t & 31, r0 = t >> 5;
+  const bool col_ok = n0 + 8 * c < N;
+#pragma unroll
+  for (int reg = 0; reg < 4; ++reg) {
+    const lds_u8* src = (reg >> 1 ? lds1 : lds0) + (reg & 1) * (kStageBytes / 2);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int r = r0 + 8 * k;  // row within the 64-row region
+      const u32x4 v = *(const lds_u32x4*)(src + r * 512 + ((c ^ (r & 31)) << 4));
+      const int grow = m0 + 64 * reg + r;
+      if (col_ok && grow < M) *(u32x4*)(p.C + (int64_t)grow * N + n0 + 8 * c) = v;
+    }
+  }
+}
+
 inline GemmParams make_params(const uint8_t* A, const fp8_scale_t* sa, const uint8_t* B, const fp8_scale_t* sb,
                               int64_t M, int64_t N, int64_t R, void* C) {
   GemmParams p;
@@ -592,6 +703,33 @@ hipError_t launch_typed(const uint8_t* A, const fp8_scale_t* sa, const uint8_t* 
   const GemmParams p = make_params(A, sa, B, sb, M, N, R, C);
   hipLaunchKernelGGL((gemm_nt_kernel<FA, FB, AMAX, TA, TB>), dim3(p.tiles_m * p.tiles_n), dim3(kThreads), 0, st,
                      p, s_out);
+  return hipGetLastError();
+}
+
+// CUs of the current device (cached per device)
+int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+template <bool TA, bool TB>
+hipError_t launch_tailsplit(const uint8_t* A, const fp8_scale_t* sa, const uint8_t* B, const fp8_scale_t* sb,
+                            int64_t M, int64_t N, int64_t R, void* C, const TailSplit& ts, float* part,
+                            hipStream_t st) {
+  constexpr int E4 = FP8_E4M3;
+  const GemmParams p = make_params(A, sa, B, sb, M, N, R, C);
+  hipLaunchKernelGGL((gemm_tailsplit_kernel<E4, E4, TA, TB>), dim3(ts.nfull + 2 * ts.ntail), dim3(kThreads), 0, st,
+                     p, ts.nfull, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(gemm_tail_fixup_kernel, dim3(ts.ntail), dim3(kThreads), 0, st, p, ts.nfull, (const float*)part);
   return hipGetLastError();
 }
 
@@ -636,6 +774,33 @@ hipError_t launch_gemm_pair(const GemmDesc& g0, const GemmDesc& g1, hipStream_t 
   hipLaunchKernelGGL((gemm_pair_kernel<E5, E4, false, false, E4, E5, true, true>), dim3(blocks), dim3(kThreads), 0,
                      st, p0, p1);
   return hipGetLastError();
+}
+
+TailSplit gemm_tail_split(int fa, int fb, int64_t M, int64_t N, int64_t R, int mode) {
+  TailSplit ts{0, 0, 0};
+  if (fa != FP8_E4M3 || fb != FP8_E4M3 || M <= 0 || N <= 0 || R < 512 || R % 256) return ts;
+  if (mode == FP8_SPLIT_NEVER || (mode == FP8_SPLIT_AUTO && R < kSplitMinR)) return ts;
+  const int64_t tiles = ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
+  const int ncu = cu_count();
+  const int64_t tail = tiles % ncu;
+  if (tail == 0 || 2 * tail > ncu) return ts;  // whole waves, or a tail too wide to split into one wave
+  ts.nfull = (int)(tiles - tail);
+  ts.ntail = (int)tail;
+  ts.bytes = (size_t)tail * 2 * 65536 * sizeof(float);
+  return ts;
+}
+
+hipError_t launch_gemm_ws(const uint8_t* A, int fa, bool ta, const fp8_scale_t* sa, const uint8_t* B, int fb,
+                          bool tb, const fp8_scale_t* sb, int64_t M, int64_t N, int64_t R, void* C, int mode,
+                          void* ws, size_t ws_bytes, hipStream_t st) {
+  const TailSplit ts = gemm_tail_split(fa, fb, M, N, R, mode);
+  if (ts.ntail == 0 || !ws || ws_bytes < ts.bytes)
+    return launch_gemm(A, fa, ta, sa, B, fb, tb, sb, M, N, R, C, st);
+  float* part = (float*)ws;
+  if (!ta && !tb) return launch_tailsplit<false, false>(A, sa, B, sb, M, N, R, C, ts, part, st);
+  if (!ta && tb) return launch_tailsplit<false, true>(A, sa, B, sb, M, N, R, C, ts, part, st);
+  if (ta && !tb) return launch_tailsplit<true, false>(A, sa, B, sb, M, N, R, C, ts, part, st);
+  return launch_tailsplit<true, true>(A, sa, B, sb, M, N, R, C, ts, part, st);
 }
 
 hipError_t launch_gemm_wgrad_amax(const uint8_t* A, bool ta, const fp8_scale_t* sa, const uint8_t* B, bool tb,

@@ -31,7 +31,7 @@ def test_header_functions_all_exported():
     for n in names:
         assert hasattr(lib, n), n
         assert n in _lib.SIGNATURES, f"binding lacks {n}"
-    assert lib.fp8_abi_version() == 8
+    assert lib.fp8_abi_version() == 9
 
 
 def test_status_strings():
@@ -116,6 +116,27 @@ def test_argument_validation_without_launch():
     assert gp(ctypes.byref(good), ctypes.byref(misaligned), None) == INV
     no_rec = _lib.GemmArgs(ok, 0, 1, None, ok, 1, 1, ok, 16, 16, 16, ok)
     assert gp(ctypes.byref(no_rec), ctypes.byref(good), None) == INV
+    # workspace GEMM: fp8_gemm's checks plus an aligned workspace; workspace size rule
+    gw = lib.fp8_gemm_ws
+    assert gw(_vp(ok), 0, 0, _vp(ok), _vp(ok), 0, 1, _vp(ok), 16, 16, 24, _vp(ok), 0, _vp(ok), 1 << 20, None) == UNS
+    assert gw(_vp(ok), 0, 0, _vp(ok), _vp(ok), 0, 1, _vp(ok), 16, 16, 16, _vp(ok), 0, _vp(ok + 8), 1 << 20,
+              None) == INV
+    assert gw(_vp(ok), 0, 0, None, _vp(ok), 0, 1, _vp(ok), 16, 16, 16, _vp(ok), 0, None, 0, None) == INV
+    assert gw(_vp(ok), 0, 0, _vp(ok), _vp(ok), 0, 1, _vp(ok), 16, 16, 16, _vp(ok), 3, None, 0, None) == INV
+    wb = lib.fp8_gemm_workspace_bytes
+    TAIL, AUTO, NEVER = _lib.FP8_SPLIT_TAIL, _lib.FP8_SPLIT_AUTO, _lib.FP8_SPLIT_NEVER
+    assert wb(0, 0, 256, 256, 1024, TAIL) == 2 * 65536 * 4      # one tile: its two halves' FP32 partials
+    assert wb(0, 0, 784, 272, 2048, TAIL) == 8 * 2 * 65536 * 4  # 4 x 2 tiles
+    assert wb(0, 0, 256, 256, 1024, AUTO) == 0                  # too short a reduction to pay
+    assert wb(0, 0, 256, 256, 16384, AUTO) == 2 * 65536 * 4
+    assert wb(0, 0, 256, 256, 16384, NEVER) == 0
+    assert wb(1, 0, 256, 256, 1024, TAIL) == 0                  # backward formats never split
+    assert wb(0, 1, 256, 256, 1024, TAIL) == 0
+    assert wb(0, 0, 256, 256, 256, TAIL) == 0                   # R below 512
+    assert wb(0, 0, 256, 256, 1040, TAIL) == 0                  # R not a multiple of 256
+    assert wb(0, 0, -16, 256, 1024, TAIL) == 0
+    assert lib.fp8_linear_scratch_bytes(256, 16384, 256) == 2 * 65536 * 4
+    assert lib.fp8_linear_scratch_bytes(256, 1024, 256) == 0
     # quantize batch: 1..4 argument sets, each checked as fp8_quantize's, distinct records
     qb = lib.fp8_quantize_batch
     QA = _lib.QuantizeArgs
