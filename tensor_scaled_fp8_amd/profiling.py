@@ -155,26 +155,30 @@ def quant_traffic_markdown(fetch_dir: str, write_dir: str, copy_bytes: int, comm
         if "cast_kernel<" in name:
             tmpl = name[name.index("cast_kernel<"):].split(">")[0] + ">"
             groups[(tmpl, ea["grid"] * 64)].append((fb, wb))
-        elif "amax_gen_kernel" in name:
-            # in fp8_quantize the cast of the same tensor is the next dispatch
+        elif "cast_batch_kernel" in name:   # the tiles of all the batch's tensors
+            groups[("cast_batch_kernel", ea["grid"] * 64)].append((fb, wb))
+        elif "amax_gen_kernel" in name or "amax_batch_kernel" in name:
+            # in fp8_quantize(_batch) the cast of the same tensors is the next dispatch
+            key = "amax_gen_kernel" if "amax_gen_kernel" in name else "amax_batch_kernel"
             nxt = fe[pairs[i + 1][0]] if i + 1 < len(pairs) else None
-            if nxt is not None and "cast_kernel<" in nxt["name"]:
-                groups[("amax_gen_kernel", nxt["grid"] * 64)].append((fb, wb))
+            if nxt is not None and ("cast_kernel<" in nxt["name"] or "cast_batch_kernel" in nxt["name"]):
+                groups[(key, nxt["grid"] * 64)].append((fb, wb))
             else:
-                groups[("amax_gen_kernel", None)].append((fb, wb))
+                groups[(key, None)].append((fb, wb))
     lines = ["# HBM traffic of the quantise kernels (amax and cast), GPT-7B-style layer", "",
              "Commands (FETCH_SIZE and WRITE_SIZE in separate runs; counters scaled by a plain "
              f"{copy_bytes}-byte device copy in the same run: fetch x{ff:.3f}, write x{wf:.3f}):", "",
              "```", command, "```", "",
              "Cast: elements = work-items x 64 (one 128 x 128 tile per 256 threads); algorithmic "
              "read 2 B/element, write 1 B per FP8 copy (2 copies when the transpose is written, "
-             "template flags <fmt, derive, count>). amax: algorithmic read = 2 B/element. A write "
+             "template flags <fmt, derive, count>; cast_batch_kernel: all tensors of one "
+             "fp8_quantize_batch call). amax: algorithmic read = 2 B/element. A write "
              "figure below the algorithmic one means lines were still dirty in the L2 when the "
              "dispatch ended; they reach HBM later, inside another dispatch's count.", "",
              "| kernel | elements | dispatches | HBM read MB | alg. read MB | read/alg | HBM write MB | "
              "write/elements (B) |", "|---|---:|---:|---:|---:|---:|---:|---:|"]
     for (k, n), v in sorted(groups.items(), key=lambda kv: (kv[0][0], kv[0][1] or 0)):
-        if k == "amax_gen_kernel" and n is None:
+        if k in ("amax_gen_kernel", "amax_batch_kernel") and n is None:
             continue  # not followed by a cast: size unknown from the counters alone
         f = sum(x[0] for x in v) / len(v)
         w = sum(x[1] for x in v) / len(v)
