@@ -182,8 +182,9 @@ typedef struct fp8_quantize_args {
 } fp8_quantize_args;
 
 /*
- * a1 + a2 + a3 for up to FP8_QUANTIZE_BATCH_MAX tensors in two kernel
- * launches (one amax pass over all of them, then all their casts), each
+ * a1 + a2 + a3 [AMAX bullets 1-4; FP8LM O1 Eq. 3 for mu] for up to
+ * FP8_QUANTIZE_BATCH_MAX tensors in two kernel launches (one amax pass
+ * over all of them, then all their casts), each
  * tensor with its own per-tensor scale exactly as fp8_quantize computes it
  * (same record fields, bit-identical FP8 bytes). For tensors that are ready
  * together, such as a linear's X and W before its forward GEMM: one launch
@@ -271,8 +272,8 @@ typedef enum {
 } fp8_split;
 
 /*
- * Workspace bytes fp8_gemm_ws uses for this GEMM on the current device
- * with this split mode: 0 when it would not split. Only E4M3 x E4M3 GEMMs
+ * Workspace bytes fp8_gemm_ws [AMAX bullet 3] uses for this GEMM on the
+ * current device with this split mode: 0 when it would not split. Only E4M3 x E4M3 GEMMs
  * (the forward) with R a multiple of 256 split: when the output tiles
  * (256 x 256) leave a last wave at most half full on the device's CUs,
  * each tile of that wave is computed as two reduction halves (FP32
@@ -286,8 +287,9 @@ typedef enum {
 size_t fp8_gemm_workspace_bytes(fp8_fmt fa, fp8_fmt fb, int64_t M, int64_t N, int64_t R, fp8_split split);
 
 /*
- * fp8_gemm with a caller workspace (same arguments, checks and result
- * bound): when fp8_gemm_workspace_bytes (same split mode) is nonzero and
+ * a4 - fp8_gemm with a caller workspace [AMAX bullet 3: the matmul on the
+ * scaled FP8 operands, the scaling undone after it] (same arguments,
+ * checks and result bound): when fp8_gemm_workspace_bytes (same split mode) is nonzero and
  * workspace_bytes covers it, the last partial wave's tiles are split as
  * described there (two launches: the GEMM and the fixup), else this is
  * fp8_gemm. split outside fp8_split -> FP8_ERR_INVALID. A split
@@ -316,8 +318,9 @@ typedef struct fp8_gemm_args {
 } fp8_gemm_args;
 
 /*
- * a5 + a6 - two GEMMs enqueued together, each computed exactly as fp8_gemm
- * computes it with the same arguments (same checks and statuses,
+ * a5 + a6 - two GEMMs enqueued together [AMAX bullets 3-4: the backward
+ * matmuls on E5 gradients and E4 weights / activations], each computed
+ * exactly as fp8_gemm computes it with the same arguments (same checks and statuses,
  * bit-identical results). When the pair is a linear's backward - first the
  * dgrad (A E5M2 ROWS, B E4M3 ROWS), then the wgrad (A E4M3 COLS, B E5M2
  * COLS) - both run in one kernel launch: the first GEMM's output tiles are
