@@ -104,23 +104,30 @@ def main():
     hip = HipEvents(torch.cuda.current_stream(dev).cuda_stream)
     events = []
 
-    def step(instrument):
-        """instrument: None, "gemm" (events around the GEMM launches) or "all"."""
+    def step(instrument, spec=False):
+        """instrument: None, "gemm" (events around the GEMM launches) or "all".
+        spec: quantise X, W and dY with fp8_quantize_spec (one pass with the
+        bias the record kept, a recast only if it changed) instead."""
         for d in lin:
             L, ws = d["L"], d["ws"]
             n = L.name
             # amax + cast to the row-major FP8 copy (2 B read twice, 1 B written);
             # the GEMMs read those copies, reduction-major where needed
+            if spec:
+                qxw = lambda: (tsf.fp8_quantize_spec(d["X"], "e4m3", ws.sx, margin, 0, ws.x8),
+                               tsf.fp8_quantize_spec(d["W"], "e4m3", ws.sw, margin, 0, ws.w8))
+                qdy = lambda: tsf.fp8_quantize_spec(d["dY"], "e5m2", ws.sdy, margin, mu, ws.dy8)
+            else:
+                qxw = lambda: tsf.fp8_quantize_batch([
+                    dict(x=d["X"], fmt="e4m3", s=ws.sx, margin=margin, out_row=ws.x8, transposed=False),
+                    dict(x=d["W"], fmt="e4m3", s=ws.sw, margin=margin, out_row=ws.w8, transposed=False)])
+                qdy = lambda: tsf.fp8_quantize(d["dY"], "e5m2", ws.sdy, margin, mu, ws.dy8, transposed=False)
             seq = [
-                ("quant", f"{n}.X+W", 5 * (L.M * L.K + L.K * L.N), 0,
-                 lambda: tsf.fp8_quantize_batch([
-                     dict(x=d["X"], fmt="e4m3", s=ws.sx, margin=margin, out_row=ws.x8, transposed=False),
-                     dict(x=d["W"], fmt="e4m3", s=ws.sw, margin=margin, out_row=ws.w8, transposed=False)])),
+                ("quant", f"{n}.X+W", 5 * (L.M * L.K + L.K * L.N), 0, qxw),
                 ("gemm", f"{n}.fwd {L.M}x{L.N}x{L.K}", 0, 2 * L.M * L.N * L.K,
                  lambda: tsf.fp8_gemm(ws.x8, "e4m3", ws.sx, ws.w8, "e4m3", ws.sw, d["Y"], "rows", "cols",
                                       workspace=ws.scratch)),
-                ("quant", f"{n}.dY", 5 * L.M * L.N, 0,
-                 lambda: tsf.fp8_quantize(d["dY"], "e5m2", ws.sdy, margin, mu, ws.dy8, transposed=False)),
+                ("quant", f"{n}.dY", 5 * L.M * L.N, 0, qdy),
                 ("gemm", f"{n}.bwd dgrad {L.M}x{L.K}x{L.N} + wgrad {L.K}x{L.N}x{L.M}", 0, 4 * L.M * L.K * L.N,
                  lambda: tsf.fp8_gemm_pair(
                      dict(a=ws.dy8, fa="e5m2", sa=ws.sdy, b=ws.w8, fb="e4m3", sb=ws.sw, out=d["dX"]),
@@ -160,12 +167,13 @@ def main():
     # and cast figures; these events cost a little time, so this pass is
     # kept out of the timed region)
     events.clear()
-    brk, infer, fp8dw, o2 = [], None, None, None
+    brk, infer, fp8dw, o2, spec = [], None, None, None, None
     if not args.step_only:
         for _ in range(args.breakdown_steps):
             step("all")
         torch.cuda.synchronize()
         brk = [(k, lb, b, f, hip.elapsed_ms(e0, e1)) for k, lb, b, f, e0, e1 in events]
+        spec = spec_pass(tsf, torch, lin, margin, mu, hip, step, args.steps, flops, wl)
         infer = inference_pass(tsf, torch, lin, margin, args.steps, args.warmup)
         fp8dw = fp8_dw_pass(tsf, torch, lin, margin, mu, args.steps, args.warmup)
         o2 = adam_pass(tsf, torch, lin, margin, mu, args.steps, args.warmup)
@@ -252,6 +260,7 @@ def main():
         "inference": infer,
         "fp8_weight_gradient": fp8dw,
         "o2_adam": o2,
+        "quantize_speculative": spec,
         "input_gen_s": round(t_gen, 1),
     }
     if check is not None:
@@ -282,6 +291,81 @@ def quantize_cold(tsf, torch, lin, margin, mu, hip, reps=3):
             t = statistics.median(ts)
             out[label] = {"us": round(t * 1e3, 1), "GB/s": round(5 * x.numel() / (t * 1e-3) / 1e9, 1)}
     del scratch
+    return out
+
+
+def spec_pass(tsf, torch, lin, margin, mu, hip, step, steps, flops, wl):
+    """fp8_quantize_spec (one pass casting with the bias the record kept,
+    then a check that recasts only if the tensor's own amax gives another
+    bias; same bytes and records as fp8_quantize) on every tensor of the
+    step: per-call time when the guess holds ("hit": 2 B read + 1 B
+    written per element) and when it is wrong ("miss", forced by presetting
+    a wrong bias outside the timed calls: 4 B read + 2 B written), against
+    the two-pass fp8_quantize (5 B). Plus the whole step with speculative
+    quantisation; the benchmark's inputs are the same every step, so there
+    every guess holds: it is the best case, reported beside the step, not
+    as it."""
+    import statistics
+    tensors = []
+    for d in lin:
+        ws, n = d["ws"], d["L"].name
+        tensors += [(f"{n}.X", d["X"], "e4m3", ws.sx, ws.x8, 0), (f"{n}.W", d["W"], "e4m3", ws.sw, ws.w8, 0),
+                    (f"{n}.dY", d["dY"], "e5m2", ws.sdy, ws.dy8, mu)]
+    miss_rec = tsf.new_scale(len(tensors))
+    biases = [tsf.read_scale(s)["bias"] for _, _, _, s, _, _ in tensors]
+    out = {}
+    for mode in ("two_pass", "hit", "miss"):
+        per, elems = [], 0
+        for i, (label, x, fmt, s, q, m) in enumerate(tensors):
+            ts = []
+            for _ in range(3):
+                if mode == "miss":
+                    tsf.fp8_scale_fixed(miss_rec[i], biases[i] + 5 if biases[i] < 100 else biases[i] - 5)
+                e0 = hip.record()
+                if mode == "two_pass":
+                    tsf.fp8_quantize(x, fmt, s, margin, m, q, transposed=False)
+                elif mode == "hit":
+                    tsf.fp8_quantize_spec(x, fmt, s, margin, m, q)
+                else:
+                    tsf.fp8_quantize_spec(x, fmt, miss_rec[i], margin, m, q)
+                e1 = hip.record()
+                torch.cuda.synchronize()
+                ts.append(hip.elapsed_ms(e0, e1))
+            per.append(statistics.median(ts))
+            elems += x.numel()
+        t = sum(per)
+        moved = {"two_pass": 5, "hit": 3, "miss": 6}[mode]
+        out[mode] = {"ms_per_step": round(t, 4), "bytes_moved_per_element": moved,
+                     "GB/s_moved": round(moved * elems / (t * 1e-3) / 1e9, 1),
+                     "elements_per_ns": round(elems / (t * 1e6), 2)}
+    for _ in range(2):
+        step(None, spec=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(None, spec=True)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    out["step_guess_holds"] = {"ms_per_step": round(ms, 4), "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 1)}
+    # does the guess hold for a new batch? Independent N(0, sigma) draws of
+    # every tensor (normal workloads only), each quantised with the record
+    # its predecessor left: a hit when the derived bias equals the guess
+    if not wl.x_outliers and not wl.dy_log_uniform:
+        g = torch.Generator(device=lin[0]["X"].device)
+        g.manual_seed(20261)
+        sig = {"X": 1.0, "W": wl.sigma_w, "dY": wl.sigma_dy}
+        hits = 0
+        for label, x, fmt, s, q, m in tensors:
+            x2 = (torch.randn(x.shape, generator=g, device=x.device) * sig[label.split(".")[1]]).to(torch.bfloat16)
+            tsf.fp8_quantize_spec(x2, fmt, s, margin, m, q)
+            w = s.cpu()
+            hits += int(w[1] == w[6])          # bias == the guess it replaced
+            tsf.fp8_quantize(x, fmt, s, margin, m, q, transposed=False)   # back to this input's record
+            del x2
+        out["independent_draws"] = {"tensors": len(tensors), "guess_held": hits}
+    out["note"] = ("one call per tensor with events around it (median of 3); miss = the record's bias preset "
+                   "wrong; step_guess_holds = the whole step with fp8_quantize_spec for X, W and dY on the "
+                   "benchmark's fixed inputs (every guess holds: the best case, not the headline)")
     return out
 
 

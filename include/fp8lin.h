@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define FP8LIN_ABI_VERSION 9
+#define FP8LIN_ABI_VERSION 10
 
 typedef enum fp8_fmt {
   FP8_E4M3 = 0, /* OCP E4M3FN: weights and activations [AMAX bullet 4] */
@@ -105,7 +105,7 @@ typedef struct fp8_scale_t {
   float scale_inv;
   uint32_t flags;
   uint32_t reduce_bits;   /* internal: running max of the |bf16| bit patterns */
-  uint32_t reserved1;     /* unused, zero */
+  int32_t spec_bias;      /* internal: the bias fp8_quantize_spec's cast guessed */
   uint32_t sat_count;     /* elements saturated by the last fp8_wgrad_fp8 cast */
   uint64_t gen_max;       /* internal: tagged running max */
   uint64_t epoch;         /* internal: tag of the last maximum consumed */
@@ -166,6 +166,21 @@ int32_t fp8_bias_host(float amax, fp8_fmt fmt, int margin, int mu_log2, uint32_t
 fp8_status fp8_quantize(const void* x_bf16, int64_t rows, int64_t cols, fp8_fmt fmt, int margin,
                         int mu_log2, fp8_scale_t* s_dev, uint8_t* out_rowwise, uint8_t* out_transposed,
                         hipStream_t stream);
+
+/*
+ * a1 + a2 + a3 [AMAX bullets 1-4] in one pass over x plus a check: the
+ * cast uses the bias the record holds from its previous quantisation (a
+ * guess) while the same pass takes max |x|; a second kernel derives the
+ * bias from that max by the rule of fp8_quantize and, only where it
+ * differs from the guess, recasts x with it. The record and every byte of
+ * out_rowwise equal fp8_quantize's (the guess only decides how much work
+ * is done): 2 B read + 1 B written per element when the bias repeats, 4 +
+ * 2 when it changes (a fresh record holds bias 0). Arguments as for
+ * fp8_quantize, row-major output only (out_rowwise required). The record
+ * must have been zeroed once; its spec_bias word is internal.
+ */
+fp8_status fp8_quantize_spec(const void* x_bf16, int64_t rows, int64_t cols, fp8_fmt fmt, int margin,
+                             int mu_log2, fp8_scale_t* s_dev, uint8_t* out_rowwise, hipStream_t stream);
 
 /* Most tensors one fp8_quantize_batch call takes. */
 #define FP8_QUANTIZE_BATCH_MAX 4

@@ -24,6 +24,7 @@ SIGNATURES = {
     "fp8_bias_host": (ctypes.c_int32, [ctypes.c_float, c_int, c_int, c_int, ctypes.POINTER(ctypes.c_uint32)]),
     "fp8_quantize": (c_int, [c_vp, c_i64, c_i64, c_int, c_int, c_int, c_vp, c_vp, c_vp, c_vp]),
     "fp8_quantize_batch": (c_int, [c_vp, c_int, c_vp]),
+    "fp8_quantize_spec": (c_int, [c_vp, c_i64, c_i64, c_int, c_int, c_int, c_vp, c_vp, c_vp]),
     "fp8_scale_fixed": (c_int, [c_vp, ctypes.c_int32, c_vp]),
     "fp8_cast": (c_int, [c_vp, c_i64, c_i64, c_int, c_vp, c_vp, c_vp, c_vp]),
     "fp8_gemm_nt": (c_int, [c_vp, c_int, c_vp, c_vp, c_int, c_vp, c_i64, c_i64, c_i64, c_vp, c_vp]),
@@ -50,7 +51,7 @@ FP8_OK, FP8_ERR_INVALID, FP8_ERR_UNSUPPORTED, FP8_ERR_HIP = 0, 1, 2, 3
 FLAG_NONFINITE, FLAG_ZERO, FLAG_CLAMPED = 1, 2, 4
 FP8_SCALING_AMAX, FP8_SCALING_FIXED = 0, 1
 FP8_SPLIT_AUTO, FP8_SPLIT_NEVER, FP8_SPLIT_TAIL = 0, 1, 2
-ABI_VERSION = 9
+ABI_VERSION = 10
 
 
 class LinearWs(ctypes.Structure):

@@ -4,6 +4,7 @@ every step of the computation runs in the HIP kernels of libfp8lin.so.
 
 Names follow the C entry points: fp8_amax, fp8_scale, fp8_amax_scale,
 fp8_scale_fixed, fp8_cast, fp8_gemm_nt, fp8_gemm, fp8_gemm_pair, fp8_quantize, fp8_quantize_batch,
+fp8_quantize_spec,
 fp8_linear_fwd,
 fp8_linear_bwd, fp8_linear_fwd_cached, fp8_wgrad_fp8, fp8_adam_init_master,
 fp8_adam_step. A scaling record (fp8_scale_t, 64
@@ -128,6 +129,22 @@ def fp8_quantize(x: torch.Tensor, fmt, s: torch.Tensor, margin: int = 0, mu_log2
                               _dev(s, torch.int32, "s"), _dev(out_row, torch.uint8, "out_row"),
                               _dev(out_t, torch.uint8, "out_t"), _stream(x)), "fp8_quantize")
     return out_row, out_t
+
+
+def fp8_quantize_spec(x: torch.Tensor, fmt, s: torch.Tensor, margin: int = 0, mu_log2: int = 0,
+                      out_row: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """fp8_quantize (row-major output) in one pass that casts with the bias
+    the record kept from its previous call, plus a check that recasts only
+    if the tensor's own amax gives another bias. Same bytes and record."""
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D")
+    rows, cols = x.shape
+    if out_row is None:
+        out_row = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    check(load().fp8_quantize_spec(_dev(x, torch.bfloat16, "x"), rows, cols, _fmt(fmt), margin, mu_log2,
+                                   _dev(s, torch.int32, "s"), _dev(out_row, torch.uint8, "out_row"), _stream(x)),
+          "fp8_quantize_spec")
+    return out_row
 
 
 def fp8_quantize_batch(tensors):

@@ -115,6 +115,14 @@ fp8_status fp8_quantize(const void* x_bf16, int64_t rows, int64_t cols, fp8_fmt 
                                     out_transposed, stream));
 }
 
+fp8_status fp8_quantize_spec(const void* x_bf16, int64_t rows, int64_t cols, fp8_fmt fmt, int margin,
+                             int mu_log2, fp8_scale_t* s_dev, uint8_t* out_rowwise, hipStream_t stream) {
+  const fp8_status st = check_quantize(x_bf16, rows, cols, fmt, margin, mu_log2, s_dev, out_rowwise, nullptr);
+  if (st != FP8_OK) return st;
+  if (rows > 0 && cols > 0 && !out_rowwise) return FP8_ERR_INVALID;
+  return hip_status(launch_quantize_spec(x_bf16, rows, cols, fmt, margin, mu_log2, s_dev, out_rowwise, stream));
+}
+
 fp8_status fp8_quantize_batch(const fp8_quantize_args* tensors, int count, hipStream_t stream) {
   if (!tensors || count < 1 || count > FP8_QUANTIZE_BATCH_MAX) return FP8_ERR_INVALID;
   static_assert(FP8_QUANTIZE_BATCH_MAX == kQuantBatchMax, "batch limit");

@@ -24,9 +24,11 @@ namespace fp8lin {
 namespace {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kTile = 128;
 constexpr int kThreads = 256;
+constexpr int64_t kSpecBlocks = 512;  // grid cap of the speculative quantise
 
 template <int FMT>
 __device__ inline uint32_t cvt4(uint32_t w0, uint32_t w1, float scale) {
@@ -258,6 +260,109 @@ __global__ __launch_bounds__(kThreads) void cast_batch_kernel(CastBatch b) {
                                      tile);
 }
 
+// Speculative a1 + a3 in one pass: each block casts its tiles (tile
+// blockIdx.x, then every gridDim.x-th) with the bias the record holds from
+// its previous quantisation (the guess; block 0 keeps it in s->spec_bias),
+// and merges the max |x| of its tiles into the tagged maximum as the amax
+// pass does (one merge per block, so the grid stays small). NaN bytes are
+// patched where a thread's patch holds a NaN (the same bytes the
+// derive-cast writes); +-inf and out-of-range values saturate, as there.
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void quantize_spec_kernel(const uint16_t* __restrict__ x, int64_t rows,
+                                                                 int64_t cols, int64_t tiles_c, int64_t ntiles,
+                                                                 fp8_scale_t* s, uint8_t* __restrict__ out_row) {
+  const int t = threadIdx.x;
+  const int rg = t >> 4, cc = t & 15;
+  const int32_t guess = s->bias;
+  const float scale = pow2f(guess);
+  uint32_t mag = 0;
+  for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+  const int64_t tr = tile / tiles_c, tc = tile - (tile / tiles_c) * tiles_c;
+  const int64_t rr = tr * kTile + 8 * rg, cx = tc * kTile + 8 * cc;
+  if (rr < rows && cx < cols) {
+    const uint16_t* src = x + rr * cols + cx;
+    u32x4 v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = __builtin_nontemporal_load((const u32x4*)(src + i * cols));
+    u16x2 m = {0, 0};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, (uint32_t)(v[i].x & 0x7FFF7FFFu)));
+      m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, (uint32_t)(v[i].y & 0x7FFF7FFFu)));
+      m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, (uint32_t)(v[i].z & 0x7FFF7FFFu)));
+      m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, (uint32_t)(v[i].w & 0x7FFF7FFFu)));
+    }
+    const uint32_t tmag = m.x > m.y ? m.x : m.y;
+    mag = tmag > mag ? tmag : mag;
+    uint32_t lo[8], hi[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      lo[i] = cvt4<FMT>(v[i].x, v[i].y, scale);
+      hi[i] = cvt4<FMT>(v[i].z, v[i].w, scale);
+    }
+    if (tmag > 0x7F80u) {  // a NaN in this thread's patch
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        lo[i] = patch_nan(lo[i], v[i].x, v[i].y);
+        hi[i] = patch_nan(hi[i], v[i].z, v[i].w);
+      }
+    }
+    uint8_t* dst = out_row + rr * cols + cx;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) *(uint2*)(dst + i * cols) = make_uint2(lo[i], hi[i]);
+  }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {  // wavefront max
+    const uint32_t o = (uint32_t)__shfl_xor((int)mag, off, 64);
+    mag = o > mag ? o : mag;
+  }
+  uint32_t* const wmax = g_wsum;
+  if ((t & 63) == 0) wmax[t >> 6] = mag;
+  __syncthreads();
+  if (t == 0) {
+    uint32_t b = wmax[0];
+#pragma unroll
+    for (int i = 1; i < kThreads / 64; ++i) b = wmax[i] > b ? wmax[i] : b;
+    const unsigned long long val = (reduction_tag(s) << 16) | b;
+    unsigned long long* word = (unsigned long long*)&s->gen_max;
+    const unsigned long long seen = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (val > seen) atomicMax(word, val);
+    if (blockIdx.x == 0) s->spec_bias = guess;
+  }
+}
+
+// The check after quantize_spec_kernel: the bias from the merged maximum
+// (the rule of fp8_quantize); block 0 publishes the record. Where it equals
+// the guess the speculative bytes are final; otherwise every block recasts
+// its tile with it (the derive-cast tile body).
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void quantize_check_kernel(const uint16_t* __restrict__ x, int64_t rows,
+                                                                  int64_t cols, int64_t tiles_c, int64_t ntiles,
+                                                                  fp8_scale_t* s, uint8_t* __restrict__ out_row,
+                                                                  int margin, int mu_log2) {
+  const unsigned long long word =
+      __hip_atomic_load((unsigned long long*)&s->gen_max, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  uint32_t flags;
+  const int32_t b = bias_from_amax_bits((uint32_t)(word & 0xFFFFu) << 16, FMT, margin, mu_log2, &flags);
+  if (b == s->spec_bias) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+      union { uint32_t u; float f; } a;
+      a.u = (uint32_t)(word & 0xFFFFu) << 16;
+      s->amax = a.f;
+      s->bias = b;
+      s->scale = pow2f(b);
+      s->scale_inv = pow2f(-b);
+      s->flags = flags;
+      s->epoch = word >> 16;
+    }
+    return;
+  }
+  // recast (the block holding tile 0 publishes the same record fields inside)
+  for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x)
+    cast_tile<FMT, true, false>(x, rows, cols, tiles_c, s, out_row, nullptr, margin, mu_log2, tile);
+}
+
 template <bool DERIVE, bool COUNT = false>
 hipError_t launch_cast_t(const void* x, int64_t rows, int64_t cols, int fmt, fp8_scale_t* s,
                          uint8_t* out_row, uint8_t* out_t, int margin, int mu_log2, hipStream_t st) {
@@ -317,6 +422,32 @@ hipError_t launch_quantize_batch(const QuantDesc* d, int count, hipStream_t st) 
     blocks += empty ? 1 : (int)(((d[i].rows + kTile - 1) / kTile) * c.tiles_c);
   }
   hipLaunchKernelGGL(cast_batch_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, st, b);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_spec(const void* x, int64_t rows, int64_t cols, int fmt, int margin, int mu_log2,
+                                fp8_scale_t* s, uint8_t* out_row, hipStream_t st) {
+  int64_t tiles_r = (rows + kTile - 1) / kTile, tiles_c = (cols + kTile - 1) / kTile;
+  if (tiles_r * tiles_c == 0) tiles_r = tiles_c = 1;  // empty: one block that reads nothing
+  const int64_t ntiles = tiles_r * tiles_c;
+  // at most kSpecBlocks blocks, each looping over tiles: one merge per block
+  const dim3 grid((unsigned)(ntiles < kSpecBlocks ? ntiles : kSpecBlocks));
+  const uint16_t* xp = (const uint16_t*)x;
+  if (fmt == FP8_E4M3) {
+    hipLaunchKernelGGL((quantize_spec_kernel<FP8_E4M3>), grid, dim3(kThreads), 0, st, xp, rows, cols, tiles_c,
+                       ntiles, s, out_row);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((quantize_check_kernel<FP8_E4M3>), grid, dim3(kThreads), 0, st, xp, rows, cols, tiles_c,
+                       ntiles, s, out_row, margin, mu_log2);
+  } else {
+    hipLaunchKernelGGL((quantize_spec_kernel<FP8_E5M2>), grid, dim3(kThreads), 0, st, xp, rows, cols, tiles_c,
+                       ntiles, s, out_row);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((quantize_check_kernel<FP8_E5M2>), grid, dim3(kThreads), 0, st, xp, rows, cols, tiles_c,
+                       ntiles, s, out_row, margin, mu_log2);
+  }
   return hipGetLastError();
 }
 

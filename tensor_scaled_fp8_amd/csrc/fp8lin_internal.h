@@ -113,6 +113,11 @@ hipError_t launch_amax_gen(const void* x, int64_t n, fp8_scale_t* s, hipStream_t
 // amax pass + cast that derives the scale (fp8_quantize)
 hipError_t launch_quantize(const void* x, int64_t rows, int64_t cols, int fmt, int margin, int mu_log2,
                            fp8_scale_t* s, uint8_t* out_row, uint8_t* out_t, hipStream_t st);
+// fp8_quantize_spec: one pass that casts with the record's current bias and
+// merges the amax, then a check that recasts only if the bias changed
+// (row-major output only)
+hipError_t launch_quantize_spec(const void* x, int64_t rows, int64_t cols, int fmt, int margin, int mu_log2,
+                                fp8_scale_t* s, uint8_t* out_row, hipStream_t st);
 // Several tensors quantised in two launches (fp8_quantize_batch).
 constexpr int kQuantBatchMax = 4;
 struct QuantDesc {

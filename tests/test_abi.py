@@ -31,7 +31,7 @@ def test_header_functions_all_exported():
     for n in names:
         assert hasattr(lib, n), n
         assert n in _lib.SIGNATURES, f"binding lacks {n}"
-    assert lib.fp8_abi_version() == 9
+    assert lib.fp8_abi_version() == 10
 
 
 def test_status_strings():
@@ -137,6 +137,13 @@ def test_argument_validation_without_launch():
     assert wb(0, 0, -16, 256, 1024, TAIL) == 0
     assert lib.fp8_linear_scratch_bytes(256, 16384, 256) == 2 * 65536 * 4
     assert lib.fp8_linear_scratch_bytes(256, 1024, 256) == 0
+    # speculative quantise: fp8_quantize's checks, row-major output required
+    qs = lib.fp8_quantize_spec
+    assert qs(_vp(ok), 16, 16, 0, 0, 0, _vp(ok), None, None) == INV
+    assert qs(_vp(ok), 16, 24, 0, 0, 0, _vp(ok), _vp(ok), None) == UNS
+    assert qs(_vp(ok), 16, 16, 2, 0, 0, _vp(ok), _vp(ok), None) == INV
+    assert qs(_vp(ok), 16, 16, 0, 0, 0, None, _vp(ok), None) == INV
+    assert qs(_vp(ok), 16, 16, 0, 0, 0, _vp(ok), _vp(ok + 4), None) == INV
     # quantize batch: 1..4 argument sets, each checked as fp8_quantize's, distinct records
     qb = lib.fp8_quantize_batch
     QA = _lib.QuantizeArgs
