@@ -48,7 +48,7 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=512, help="token rows of the CPU oracle sample")
     ap.add_argument("--cpu-cols", type=int, default=6144, help="output features of the CPU oracle sample")
     ap.add_argument("--check", action="store_true", help="check sampled outputs against the oracle")
-    ap.add_argument("--breakdown-steps", type=int, default=3,
+    ap.add_argument("--breakdown-steps", type=int, default=5,
                     help="extra steps with events around every launch (amax/cast figures)")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "gemm_traffic_gpt7b-layer.json"),
                     help="JSON file with measured per-launch HBM bytes of the GEMM kernel")
@@ -195,15 +195,22 @@ def main():
                 "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4), "traffic": traffic,
                 "kernel": "gemm_nt_kernel (forward) + gemm_pair_kernel (dgrad + wgrad), FP8 MFMA",
                 "avg_launch_us": round(g["ms"] * 1e3 / g["n"], 2)}
-    agg = aggregate(brk)
     kernels = {}
-    if "quant" in agg:
-        a = agg["quant"]
-        gbs = a["bytes"] / (a["ms"] * 1e-3) / 1e9
+    # per call: the median over the breakdown steps (one slow call, e.g. a
+    # host hiccup between two events, would otherwise skew the sum)
+    import statistics
+    qcalls = {}
+    for kind, label, nbytes, _, t in brk:
+        if kind == "quant":
+            qcalls.setdefault(label, [nbytes, []])[1].append(t)
+    if qcalls:
+        q_ms = sum(statistics.median(ts) for _, ts in qcalls.values())
+        q_bytes = sum(nb for nb, _ in qcalls.values())
+        gbs = q_bytes / (q_ms * 1e-3) / 1e9
         kernels["amax+cast"] = {"GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
-                                "ms_per_step": round(a["ms"] / args.breakdown_steps, 4),
-                                "avg_call_us": round(a["ms"] * 1e3 / a["n"], 2),
-                                "bytes": "5 per element: amax read 2, cast read 2, row-major FP8 copy 1"}
+                                "ms_per_step": round(q_ms, 4), "avg_call_us": round(q_ms * 1e3 / len(qcalls), 2),
+                                "bytes": "5 per element: amax read 2, cast read 2, row-major FP8 copy 1",
+                                "timing": f"median per call over {args.breakdown_steps} steps"}
     kernels["gemm"] = {"TFLOP/s": round(gemm_tflops, 1), "ms_per_step": round(g["ms"] / args.steps, 4)}
     per = {}
     for kind, label, _, fl, t in timed:
@@ -214,14 +221,9 @@ def main():
     kernels["gemm_by_launch"] = {lb: {"us": round(t * 1e3 / n, 1), "TFLOP/s": round(fl / (t / n * 1e-3) / 1e12, 1)}
                                  for lb, (t, n, fl) in per.items()}
     # per tensor (warm, inside the step) and per linear (6*M*K*N over its three GEMMs)
-    qt = {}
-    for kind, label, nbytes, _, t in brk:
-        if kind == "quant":
-            q = qt.setdefault(label, [0.0, 0, nbytes])
-            q[0] += t
-            q[1] += 1
-    kernels["amax+cast_by_tensor"] = {lb: {"us": round(t * 1e3 / n, 1), "GB/s": round(b / (t / n * 1e-3) / 1e9, 1)}
-                                      for lb, (t, n, b) in qt.items()}
+    kernels["amax+cast_by_tensor"] = {lb: {"us": round(statistics.median(ts) * 1e3, 1),
+                                           "GB/s": round(nb / (statistics.median(ts) * 1e-3) / 1e9, 1)}
+                                      for lb, (nb, ts) in qcalls.items()}
     lt = {}
     for kind, label, _, fl, t in timed:
         if kind == "gemm":
@@ -232,9 +234,9 @@ def main():
                                      "TFLOP/s": round(f / (t * 1e-3) / 1e12, 1)} for n, (t, f) in lt.items()}
     if not args.step_only:
         kernels["amax+cast_cold"] = quantize_cold(tsf, torch, lin, margin, mu, hip)
-    kernels["note"] = ("gemm: events in the timed region; amax+cast (fp8_quantize: amax pass + "
-                       f"cast kernel): a separate pass of {args.breakdown_steps} steps with events "
-                       "around every call")
+    kernels["note"] = ("gemm: events in the timed region; amax+cast (fp8_quantize / fp8_quantize_batch: "
+                       f"amax pass + cast kernel): a separate pass of {args.breakdown_steps} steps with events "
+                       "around every call, median per call")
 
     check = None
     if args.check:

@@ -29,6 +29,7 @@ typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 constexpr int kTile = 128;
 constexpr int kThreads = 256;
 constexpr int64_t kSpecBlocks = 512;  // grid cap of the speculative quantise
+constexpr int kSpecTiles = 4;         // tiles whose loads one speculative step keeps in flight
 
 template <int FMT>
 __device__ inline uint32_t cvt4(uint32_t w0, uint32_t w1, float scale) {
@@ -78,6 +79,13 @@ __device__ inline void transpose4(const uint32_t in[4], uint32_t out[4]) {
   out[3] = __builtin_amdgcn_perm(b1, a1, 0x07060302u);
 }
 
+// The tagged maximum the reduction before this kernel merged. It is final
+// while this kernel runs (only a later reduction changes it), so a plain
+// load of the uniform address does: one request per wave, where a
+// device-scope atomic load per thread (a thousand blocks of 256 threads on
+// one address) measured ~3 us per launch.
+__device__ inline unsigned long long merged_max(const fp8_scale_t* s) { return s->gen_max; }
+
 // LDS of a cast block, declared once for the file so that a kernel holding
 // both format variants (the batch kernel) still needs only this much.
 __shared__ uint4 g_tile[kTile * kTile / 16];  // transposed tile: 128 rows of 128 bytes
@@ -105,8 +113,7 @@ __device__ __forceinline__ void cast_tile(const uint16_t* __restrict__ x, int64_
   bool nonfinite;
   uint32_t sat_above = 0x7F80u;  // COUNT: magnitudes above this (and <= inf) saturate
   if constexpr (DERIVE) {
-    const unsigned long long word =
-        __hip_atomic_load((unsigned long long*)&s->gen_max, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned long long word = merged_max(s);
     const uint32_t mag = (uint32_t)(word & 0xFFFFu);
     uint32_t flags;
     const int32_t b = bias_from_amax_bits(mag << 16, FMT, margin, mu_log2, &flags);
@@ -261,7 +268,7 @@ __global__ __launch_bounds__(kThreads) void cast_batch_kernel(CastBatch b) {
 }
 
 // Speculative a1 + a3 in one pass: each block casts its tiles (tile
-// blockIdx.x, then every gridDim.x-th) with the bias the record holds from
+// blockIdx.x, then every gridDim.x-th, kSpecTiles at a time) with the bias the record holds from
 // its previous quantisation (the guess; block 0 keeps it in s->spec_bias),
 // and merges the max |x| of its tiles into the tagged maximum as the amax
 // pass does (one merge per block, so the grid stays small). NaN bytes are
@@ -276,41 +283,56 @@ __global__ __launch_bounds__(kThreads) void quantize_spec_kernel(const uint16_t*
   const int32_t guess = s->bias;
   const float scale = pow2f(guess);
   uint32_t mag = 0;
-  for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-  const int64_t tr = tile / tiles_c, tc = tile - (tile / tiles_c) * tiles_c;
-  const int64_t rr = tr * kTile + 8 * rg, cx = tc * kTile + 8 * cc;
-  if (rr < rows && cx < cols) {
-    const uint16_t* src = x + rr * cols + cx;
-    u32x4 v[8];
+  // kSpecTiles tiles per step (tiles b, b + G, ..., G = gridDim.x): all
+  // their loads are issued before any is converted, so a CU keeps as many
+  // bytes in flight as the cast kernel's many resident blocks do
+  const int64_t G = gridDim.x;
+  for (int64_t base = blockIdx.x; base < ntiles; base += kSpecTiles * G) {
+    u32x4 v[kSpecTiles][8];
+    int64_t off[kSpecTiles];
+    bool ok[kSpecTiles];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = __builtin_nontemporal_load((const u32x4*)(src + i * cols));
-    u16x2 m = {0, 0};
+    for (int j = 0; j < kSpecTiles; ++j) {
+      const int64_t tile = base + j * G;
+      const int64_t tr = tile / tiles_c, tc = tile - (tile / tiles_c) * tiles_c;
+      const int64_t rr = tr * kTile + 8 * rg, cx = tc * kTile + 8 * cc;
+      ok[j] = tile < ntiles && rr < rows && cx < cols;
+      off[j] = rr * cols + cx;
+      if (ok[j]) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, (uint32_t)(v[i].x & 0x7FFF7FFFu)));
-      m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, (uint32_t)(v[i].y & 0x7FFF7FFFu)));
-      m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, (uint32_t)(v[i].z & 0x7FFF7FFFu)));
-      m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, (uint32_t)(v[i].w & 0x7FFF7FFFu)));
-    }
-    const uint32_t tmag = m.x > m.y ? m.x : m.y;
-    mag = tmag > mag ? tmag : mag;
-    uint32_t lo[8], hi[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      lo[i] = cvt4<FMT>(v[i].x, v[i].y, scale);
-      hi[i] = cvt4<FMT>(v[i].z, v[i].w, scale);
-    }
-    if (tmag > 0x7F80u) {  // a NaN in this thread's patch
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        lo[i] = patch_nan(lo[i], v[i].x, v[i].y);
-        hi[i] = patch_nan(hi[i], v[i].z, v[i].w);
+        for (int i = 0; i < 8; ++i) v[j][i] = __builtin_nontemporal_load((const u32x4*)(x + off[j] + i * cols));
       }
     }
-    uint8_t* dst = out_row + rr * cols + cx;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) *(uint2*)(dst + i * cols) = make_uint2(lo[i], hi[i]);
-  }
+    for (int j = 0; j < kSpecTiles; ++j) {
+      if (!ok[j]) continue;
+      u16x2 m = {0, 0};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, (uint32_t)(v[j][i].x & 0x7FFF7FFFu)));
+        m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, (uint32_t)(v[j][i].y & 0x7FFF7FFFu)));
+        m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, (uint32_t)(v[j][i].z & 0x7FFF7FFFu)));
+        m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, (uint32_t)(v[j][i].w & 0x7FFF7FFFu)));
+      }
+      const uint32_t tmag = m.x > m.y ? m.x : m.y;
+      mag = tmag > mag ? tmag : mag;
+      uint32_t lo[8], hi[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        lo[i] = cvt4<FMT>(v[j][i].x, v[j][i].y, scale);
+        hi[i] = cvt4<FMT>(v[j][i].z, v[j][i].w, scale);
+      }
+      if (tmag > 0x7F80u) {  // a NaN in this thread's patch
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          lo[i] = patch_nan(lo[i], v[j][i].x, v[j][i].y);
+          hi[i] = patch_nan(hi[i], v[j][i].z, v[j][i].w);
+        }
+      }
+      uint8_t* dst = out_row + off[j];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) *(uint2*)(dst + i * cols) = make_uint2(lo[i], hi[i]);
+    }
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {  // wavefront max
@@ -341,8 +363,7 @@ __global__ __launch_bounds__(kThreads) void quantize_check_kernel(const uint16_t
                                                                   int64_t cols, int64_t tiles_c, int64_t ntiles,
                                                                   fp8_scale_t* s, uint8_t* __restrict__ out_row,
                                                                   int margin, int mu_log2) {
-  const unsigned long long word =
-      __hip_atomic_load((unsigned long long*)&s->gen_max, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const unsigned long long word = merged_max(s);
   uint32_t flags;
   const int32_t b = bias_from_amax_bits((uint32_t)(word & 0xFFFFu) << 16, FMT, margin, mu_log2, &flags);
   if (b == s->spec_bias) {
