@@ -171,6 +171,12 @@ def test_argument_validation_without_launch():
     # the transposed copies are optional, but aligned when given
     ws_mis = _lib.LinearWs(ok, ok + 4, ok, None, ok, None, ok, ok, ok)
     assert lib.fp8_linear_fwd(_vp(ok), _vp(ok), 16, 16, 16, 0, ctypes.byref(ws_mis), _vp(ok), None) == INV
+    # X and W quantised in one batch: their records must differ
+    ws_same = _lib.LinearWs(ok, None, ok, None, ok, None, ok, ok, ok + 64)
+    assert lib.fp8_linear_fwd(_vp(ok), _vp(ok), 16, 16, 16, 0, ctypes.byref(ws_same), _vp(ok), None) == INV
+    # the forward's scratch is optional, but aligned when given
+    ws_scr = _lib.LinearWs(ok, None, ok, None, ok, None, ok, ok + 64, ok + 128, ok + 8, 1 << 20)
+    assert lib.fp8_linear_fwd(_vp(ok), _vp(ok), 16, 16, 16, 0, ctypes.byref(ws_scr), _vp(ok), None) == INV
     ws_nox = _lib.LinearWs(None, None, ok, None, ok, None, ok, ok, ok)
     assert lib.fp8_linear_fwd(_vp(ok), _vp(ok), 16, 16, 16, 0, ctypes.byref(ws_nox), _vp(ok), None) == INV
     # fixed bias: only [-126, 126]
