@@ -18,6 +18,12 @@
 // tile out as 16-byte stores, 128 contiguous bytes per output row, so both
 // outputs are written in whole 128-byte lines. LDS chunks are XOR-swizzled
 // by (row / 8) so the 8-byte column writes spread over the banks.
+//
+// Also here: the casts of several tensors in one launch (cast_batch_kernel,
+// fp8_quantize_batch), and the speculative one-pass quantise
+// (quantize_spec_kernel casting with the record's previous bias while
+// taking the amax, quantize_check_kernel recasting only if the bias
+// changed; fp8_quantize_spec).
 #include "fp8lin_internal.h"
 
 namespace fp8lin {

@@ -51,6 +51,12 @@
 //  * Rows past M or N read a clamped (valid) row and are never stored; k
 //    past R is zero-filled in LDS, so any M, N, R that are multiples of 16
 //    work.
+//  * The per-tile body is one force-inlined function, so a launch can run
+//    tiles of two GEMMs (gemm_pair_kernel: a linear's dgrad then its
+//    wgrad, whose tiles fill the dgrad's last wave) or split the tiles of a
+//    last wave at most half full into two reduction halves
+//    (gemm_tailsplit_kernel: FP32 partials in a caller workspace, added by
+//    gemm_tail_fixup_kernel), with the per-tile arithmetic unchanged.
 #include <type_traits>
 
 #include "fp8lin_internal.h"
