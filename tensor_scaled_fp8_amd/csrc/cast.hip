@@ -34,8 +34,9 @@ typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kTile = 128;
 constexpr int kThreads = 256;
-constexpr int64_t kSpecBlocks = 512;  // grid cap of the speculative quantise
-constexpr int kSpecTiles = 4;         // tiles whose loads one speculative step keeps in flight
+constexpr int64_t kSpecBlocks = 512;  // grid cap of the speculative quantise (one merge per block)
+constexpr int kSpecGroups = 4;        // 256-thread tile groups per speculative block
+constexpr int kSpecTiles = 2;         // tiles whose loads one group step keeps in flight
 
 template <int FMT>
 __device__ inline uint32_t cvt4(uint32_t w0, uint32_t w1, float scale) {
@@ -281,19 +282,20 @@ __global__ __launch_bounds__(kThreads) void cast_batch_kernel(CastBatch b) {
 // patched where a thread's patch holds a NaN (the same bytes the
 // derive-cast writes); +-inf and out-of-range values saturate, as there.
 template <int FMT>
-__global__ __launch_bounds__(kThreads) void quantize_spec_kernel(const uint16_t* __restrict__ x, int64_t rows,
-                                                                 int64_t cols, int64_t tiles_c, int64_t ntiles,
-                                                                 fp8_scale_t* s, uint8_t* __restrict__ out_row) {
+__global__ __launch_bounds__(kThreads * kSpecGroups) void quantize_spec_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t tiles_c, int64_t ntiles, fp8_scale_t* s,
+    uint8_t* __restrict__ out_row) {
   const int t = threadIdx.x;
-  const int rg = t >> 4, cc = t & 15;
+  const int rg = (t & (kThreads - 1)) >> 4, cc = t & 15;
   const int32_t guess = s->bias;
   const float scale = pow2f(guess);
   uint32_t mag = 0;
-  // kSpecTiles tiles per step (tiles b, b + G, ..., G = gridDim.x): all
-  // their loads are issued before any is converted, so a CU keeps as many
-  // bytes in flight as the cast kernel's many resident blocks do
-  const int64_t G = gridDim.x;
-  for (int64_t base = blockIdx.x; base < ntiles; base += kSpecTiles * G) {
+  // each 256-thread group takes kSpecTiles tiles per step (tiles g, g + G,
+  // ..., G = the grid's group count) and issues all their loads before it
+  // converts any; four groups per block keep many waves resident per CU
+  // while the number of blocks, and so of merges, stays small
+  const int64_t G = (int64_t)gridDim.x * kSpecGroups;
+  for (int64_t base = (int64_t)blockIdx.x * kSpecGroups + (t >> 8); base < ntiles; base += kSpecTiles * G) {
     u32x4 v[kSpecTiles][8];
     int64_t off[kSpecTiles];
     bool ok[kSpecTiles];
@@ -345,13 +347,13 @@ __global__ __launch_bounds__(kThreads) void quantize_spec_kernel(const uint16_t*
     const uint32_t o = (uint32_t)__shfl_xor((int)mag, off, 64);
     mag = o > mag ? o : mag;
   }
-  uint32_t* const wmax = g_wsum;
+  __shared__ uint32_t wmax[kThreads * kSpecGroups / 64];
   if ((t & 63) == 0) wmax[t >> 6] = mag;
   __syncthreads();
   if (t == 0) {
     uint32_t b = wmax[0];
 #pragma unroll
-    for (int i = 1; i < kThreads / 64; ++i) b = wmax[i] > b ? wmax[i] : b;
+    for (int i = 1; i < kThreads * kSpecGroups / 64; ++i) b = wmax[i] > b ? wmax[i] : b;
     const unsigned long long val = (reduction_tag(s) << 16) | b;
     unsigned long long* word = (unsigned long long*)&s->gen_max;
     const unsigned long long seen = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -457,19 +459,23 @@ hipError_t launch_quantize_spec(const void* x, int64_t rows, int64_t cols, int f
   int64_t tiles_r = (rows + kTile - 1) / kTile, tiles_c = (cols + kTile - 1) / kTile;
   if (tiles_r * tiles_c == 0) tiles_r = tiles_c = 1;  // empty: one block that reads nothing
   const int64_t ntiles = tiles_r * tiles_c;
-  // at most kSpecBlocks blocks, each looping over tiles: one merge per block
+  // at most kSpecBlocks blocks of kSpecGroups tile groups, looping over
+  // tiles: one merge per block. The check runs one block per tile up to
+  // the same cap (it only recasts when the guess was wrong).
+  const int64_t sblocks = (ntiles + kSpecGroups - 1) / kSpecGroups;
+  const dim3 sgrid((unsigned)(sblocks < kSpecBlocks ? sblocks : kSpecBlocks));
   const dim3 grid((unsigned)(ntiles < kSpecBlocks ? ntiles : kSpecBlocks));
   const uint16_t* xp = (const uint16_t*)x;
   if (fmt == FP8_E4M3) {
-    hipLaunchKernelGGL((quantize_spec_kernel<FP8_E4M3>), grid, dim3(kThreads), 0, st, xp, rows, cols, tiles_c,
-                       ntiles, s, out_row);
+    hipLaunchKernelGGL((quantize_spec_kernel<FP8_E4M3>), sgrid, dim3(kThreads * kSpecGroups), 0, st, xp, rows,
+                       cols, tiles_c, ntiles, s, out_row);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((quantize_check_kernel<FP8_E4M3>), grid, dim3(kThreads), 0, st, xp, rows, cols, tiles_c,
                        ntiles, s, out_row, margin, mu_log2);
   } else {
-    hipLaunchKernelGGL((quantize_spec_kernel<FP8_E5M2>), grid, dim3(kThreads), 0, st, xp, rows, cols, tiles_c,
-                       ntiles, s, out_row);
+    hipLaunchKernelGGL((quantize_spec_kernel<FP8_E5M2>), sgrid, dim3(kThreads * kSpecGroups), 0, st, xp, rows,
+                       cols, tiles_c, ntiles, s, out_row);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((quantize_check_kernel<FP8_E5M2>), grid, dim3(kThreads), 0, st, xp, rows, cols, tiles_c,
