@@ -31,9 +31,9 @@
 namespace fp8lin {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 1024;        // 16 waves per block: many resident waves, few blocks
 constexpr int kVec = 8;           // elements per thread per iteration
-constexpr int kMaxBlocks = 2048;
+constexpr int kMaxBlocks = 512;      // one max merge per block and record
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
