@@ -581,38 +581,44 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, fp8_sca
   using M0 = std::integral_constant<int, 0>;
   using M2 = std::integral_constant<int, 2>;
   stage(M0{});
-  if constexpr (AMAX) {
-    // the running max stays live through the whole staging, so this
-    // variant stages both halves before it writes any (no overlap: the
-    // overlapped order needs one register more than the file holds)
-    stage(M2{});
-    // rows past M and columns past N repeat valid rows / columns (clamped
-    // operand rows), so the tile max is a max over real outputs
+  // AMAX: rows past M and columns past N repeat valid rows / columns
+  // (clamped operand rows), so the tile max is a max over real outputs.
+  // The first half's wave maximum is parked in LDS, so the running max is
+  // not live across the first half's stores.
+  auto wave_max = [&]() -> uint32_t {
     uint32_t r = cmax.x > cmax.y ? cmax.x : cmax.y;
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) {
       const uint32_t o = (uint32_t)__shfl_xor((int)r, off, 64);
       r = o > r ? o : r;
     }
-    __shared__ uint32_t wmax[kThreads / 64];
-    if (lane == 0) wmax[w] = r;
-    block_sync_lds();
+    return r;
+  };
+  __shared__ uint32_t wmax[2][kThreads / 64];
+  if constexpr (AMAX) {
+    const uint32_t r = wave_max();
+    if (lane == 0) wmax[0][w] = r;
+    cmax = (u16x2){0, 0};
+  }
+  block_sync_lds();
+  drain_pair(slot(S0{}), 0, slot(S1{}), 2);
+  stage(M2{});
+  if constexpr (AMAX) {
+    const uint32_t r = wave_max();
+    if (lane == 0) wmax[1][w] = r > wmax[0][w] ? r : wmax[0][w];
+  }
+  block_sync_lds();
+  if constexpr (AMAX) {
     if (t == 0) {
-      uint32_t b = wmax[0];
+      uint32_t b = wmax[1][0];
 #pragma unroll
-      for (int i = 1; i < kThreads / 64; ++i) b = wmax[i] > b ? wmax[i] : b;
+      for (int i = 1; i < kThreads / 64; ++i) b = wmax[1][i] > b ? wmax[1][i] : b;
       const unsigned long long v = (reduction_tag(s_out) << 16) | b;
       unsigned long long* word = (unsigned long long*)&s_out->gen_max;
       const unsigned long long seen = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (v > seen) atomicMax(word, v);
       if (tile == 0) s_out->sat_count = 0u;
     }
-    drain_pair(slot(S0{}), 0, slot(S1{}), 2);
-  } else {
-    block_sync_lds();
-    drain_pair(slot(S0{}), 0, slot(S1{}), 2);
-    stage(M2{});
-    block_sync_lds();
   }
   drain_pair(slot(S0{}) + kStageBytes / 2, 1, slot(S1{}) + kStageBytes / 2, 3);
 }
