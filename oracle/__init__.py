@@ -24,8 +24,12 @@ to [-126, 126]; the scale is 2^bias; outputs are bf16 rounded once to
 nearest even.
 
 Parity status: every function here is pinned by the `-m "not gpu"` tests in
-tests/test_oracle_*.py. The mu update policy is not defined by the pages and
-is not implemented (mu is an input).
+tests/test_oracle_*.py, the compositions too: linear_fwd_bwd's routing of
+the margin (all three tensors) and of mu (dY only) in test_oracle_linear.py,
+adam.adam_step against a hand-written scalar AdamW with field-level decode,
+closed-form biases and brute-force encoders in test_oracle_adam.py. The mu
+update policy is not defined by the pages and is not implemented here (mu
+is an input).
 """
 from .formats import E4M3, E5M2, FORMATS, Fp8Format, decode_code, decode_table, encode
 from .bf16 import bf16_to_f64, f64_to_bf16_rne, bf16_ulp
