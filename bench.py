@@ -2,9 +2,10 @@
 """Benchmark: one per-tensor dynamically scaled FP8 transformer layer's
 linears, forward + backward, on one MI355X.
 
-A step runs, for every linear of the layer (default: the GPT-7B-style
-layer, 4096 tokens, hidden 4096: qkv 4096->12288, proj 4096->4096,
-up 4096->16384, down 16384->4096):
+A step runs, for every linear of the layer (default: the GPT-175B-style
+layer at full width, 2048 tokens, hidden 12288: qkv 12288->36864,
+proj 12288->12288, up 12288->49152, down 49152->12288, the largest of the
+layer workloads):
     quantize(X), quantize(W)   amax + scale + cast to row-major FP8 (E4M3),
                                both tensors in one launch pair (fp8_quantize_batch)
     Y  = FP8 GEMM (x8, w8 read reduction-major; a last wave at most half
@@ -17,11 +18,14 @@ with inputs resident in HBM.
 
 Prints ONE JSON line: value = sum over linears of 6*M*K*N / step time
 (TFLOP/s). HIP events (fence-free) around every GEMM launch of the timed
-steps give the GEMM durations: `roofline` reports the FP8 GEMM kernel (the
-dominant one) against the dense FP8 MFMA peak. A short extra pass with
-events around every launch gives the amax and cast figures (`kernels`,
-against HBM bandwidth). `cpu_baseline` times the oracle on a bounded
-sample of the same layer on the host cores."""
+steps give the GEMM durations: `roofline` reports the dominant kernel, the
+backward pair (gemm_pair_kernel: a linear's dgrad + wgrad in one launch),
+against the dense FP8 MFMA peak; `kernels.gemm` has all GEMM launches and
+the forward kernel. A short extra pass with events around every launch
+gives the amax and cast figures (`kernels`, against HBM bandwidth).
+`other_workloads` repeats the step, GEMM and amax+cast figures on the
+GPT-7B-style layer. `cpu_baseline` times the oracle on a bounded sample of
+the same layer on the host cores."""
 from __future__ import annotations
 
 import argparse
@@ -43,72 +47,68 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", type=int, default=2, help="layer workload index (1-5)")
+    ap.add_argument("--workload", type=int, default=4,
+                    help="layer workload index (1-5); default 4, the GPT-175B-style layer (the largest)")
+    ap.add_argument("--side-workloads", default="2",
+                    help="comma-separated workloads also measured (step, GEMM and amax+cast) under "
+                         "'other_workloads'; empty for none")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=512, help="token rows of the CPU oracle sample")
-    ap.add_argument("--cpu-cols", type=int, default=6144, help="output features of the CPU oracle sample")
+    ap.add_argument("--cpu-cols", type=int, default=3072, help="output features of the CPU oracle sample")
     ap.add_argument("--check", action="store_true", help="check sampled outputs against the oracle")
     ap.add_argument("--breakdown-steps", type=int, default=5,
                     help="extra steps with events around every launch (amax/cast figures)")
-    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "gemm_traffic_gpt7b-layer.json"),
-                    help="JSON file with measured per-launch HBM bytes of the GEMM kernel")
+    ap.add_argument("--traffic-dir", default=os.path.join(ROOT, "profiles"),
+                    help="directory of gemm_traffic_<workload>.json counter summaries")
     ap.add_argument("--calibration-copy", type=int, default=0,
                     help="bytes of one plain device copy run before timing (PMC calibration)")
     ap.add_argument("--step-only", action="store_true",
-                    help="only the warm-up and timed steps (for profiler runs): no breakdown, inference, "
-                         "FP8 weight-gradient, Adam or cold-cache passes")
+                    help="only the warm-up and timed steps (for profiler runs): no breakdown, side "
+                         "workloads, inference, FP8 weight-gradient, Adam or cold-cache passes")
     return ap.parse_args()
 
 
-def main():
-    args = parse()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(run with --gpus 1)", file=sys.stderr)
-        sys.exit(2)
+DOMINANT = "gemm_pair_kernel"   # dgrad + wgrad in one launch: the kernel with the largest share of the step
 
-    import numpy as np
-    import torch
-    import tensor_scaled_fp8_amd as tsf
-    from workloads import linear_inputs, workload
 
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(2)
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    tsf.load()
-    wl = workload(args.workload)
+class Layer:
+    """Device tensors of one layer workload and its step (the launches
+    fp8_linear_fwd / fp8_linear_bwd make, through the primitive entry
+    points), with HIP events around the GEMM launches (or every launch)."""
 
-    def up(bits):
-        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    def __init__(self, tsf, torch, np, wl, dev, hip, cpu_rows=0, cpu_cols=0):
+        from workloads import linear_inputs
+        self.tsf, self.torch, self.wl, self.hip = tsf, torch, wl, hip
+        self.margin, self.mu = wl.margin, wl.mu_log2
+        self.events = []
+        self.sample = []   # host slices for the CPU oracle sample
 
-    lin = []
-    t_gen = time.perf_counter()
-    for li, L in enumerate(wl.linears):
-        X, W, dY = linear_inputs(wl, li)
-        d = dict(L=L, X=up(X), W=up(W), dY=up(dY))
-        del X, W, dY
-        d["ws"] = tsf.LinearWorkspace(L.M, L.K, L.N, dev)
-        d["Y"] = torch.empty((L.M, L.N), dtype=torch.bfloat16, device=dev)
-        d["dX"] = torch.empty((L.M, L.K), dtype=torch.bfloat16, device=dev)
-        d["dW"] = torch.empty((L.K, L.N), dtype=torch.bfloat16, device=dev)
-        lin.append(d)
-    t_gen = time.perf_counter() - t_gen
-    margin, mu = wl.margin, wl.mu_log2
+        def up(bits):
+            return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
 
-    # kernel-level step: the same launches fp8_linear_fwd/bwd make. Timing
-    # events are HIP events created once, without the system-scope fence on
-    # record (a fenced timing event writes back and invalidates the caches
-    # and measurably slows the kernels around it).
-    hip = HipEvents(torch.cuda.current_stream(dev).cuda_stream)
-    events = []
+        self.lin = []
+        t = time.perf_counter()
+        for li, L in enumerate(wl.linears):
+            X, W, dY = linear_inputs(wl, li)
+            if cpu_rows:
+                n = min(cpu_cols, L.N)
+                self.sample.append((np.ascontiguousarray(X[:cpu_rows]), np.ascontiguousarray(W[:, :n]),
+                                    np.ascontiguousarray(dY[:cpu_rows, :n])))
+            d = dict(L=L, X=up(X), W=up(W), dY=up(dY))
+            del X, W, dY
+            d["ws"] = tsf.LinearWorkspace(L.M, L.K, L.N, dev)
+            d["Y"] = torch.empty((L.M, L.N), dtype=torch.bfloat16, device=dev)
+            d["dX"] = torch.empty((L.M, L.K), dtype=torch.bfloat16, device=dev)
+            d["dW"] = torch.empty((L.K, L.N), dtype=torch.bfloat16, device=dev)
+            self.lin.append(d)
+        self.gen_s = time.perf_counter() - t
 
-    def step(instrument, spec=False):
+    def step(self, instrument, spec=False):
         """instrument: None, "gemm" (events around the GEMM launches) or "all".
         spec: quantise X, W and dY with fp8_quantize_spec (one pass with the
         bias the record kept, a recast only if it changed) instead."""
-        for d in lin:
+        tsf, margin, mu, hip = self.tsf, self.margin, self.mu, self.hip
+        for d in self.lin:
             L, ws = d["L"], d["ws"]
             n = L.name
             # amax + cast to the row-major FP8 copy (2 B read twice, 1 B written);
@@ -124,23 +124,125 @@ def main():
                 qdy = lambda: tsf.fp8_quantize(d["dY"], "e5m2", ws.sdy, margin, mu, ws.dy8, transposed=False)
             seq = [
                 ("quant", f"{n}.X+W", 5 * (L.M * L.K + L.K * L.N), 0, qxw),
-                ("gemm", f"{n}.fwd {L.M}x{L.N}x{L.K}", 0, 2 * L.M * L.N * L.K,
+                ("fwd", f"{n}.fwd {L.M}x{L.N}x{L.K}", 0, 2 * L.M * L.N * L.K,
                  lambda: tsf.fp8_gemm(ws.x8, "e4m3", ws.sx, ws.w8, "e4m3", ws.sw, d["Y"], "rows", "cols",
                                       workspace=ws.scratch)),
                 ("quant", f"{n}.dY", 5 * L.M * L.N, 0, qdy),
-                ("gemm", f"{n}.bwd dgrad {L.M}x{L.K}x{L.N} + wgrad {L.K}x{L.N}x{L.M}", 0, 4 * L.M * L.K * L.N,
+                ("pair", f"{n}.bwd dgrad {L.M}x{L.K}x{L.N} + wgrad {L.K}x{L.N}x{L.M}", 0, 4 * L.M * L.K * L.N,
                  lambda: tsf.fp8_gemm_pair(
                      dict(a=ws.dy8, fa="e5m2", sa=ws.sdy, b=ws.w8, fb="e4m3", sb=ws.sw, out=d["dX"]),
                      dict(a=ws.x8, fa="e4m3", sa=ws.sx, b=ws.dy8, fb="e5m2", sb=ws.sdy, out=d["dW"],
                           a_layout="cols", b_layout="cols"))),
             ]
             for kind, label, nbytes, flops, fn in seq:
-                if instrument == "all" or (instrument == "gemm" and kind == "gemm"):
+                if instrument == "all" or (instrument == "gemm" and kind != "quant"):
                     e0 = hip.record()
                     fn()
-                    events.append((kind, label, nbytes, flops, e0, hip.record()))
+                    self.events.append((kind, label, nbytes, flops, e0, hip.record()))
                 else:
                     fn()
+
+    def collect(self):
+        rows = [(k, lb, b, f, self.hip.elapsed_ms(e0, e1)) for k, lb, b, f, e0, e1 in self.events]
+        self.events.clear()
+        return rows
+
+    def timed(self, steps, warmup):
+        """warmup untimed steps, then steps timed (events around the GEMMs)."""
+        torch = self.torch
+        for _ in range(warmup):
+            self.step(None)
+        self.hip.reserve(self.hip.next + 2 * 2 * len(self.lin) * steps + 64)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            self.step("gemm")
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+        return ms, self.collect()
+
+    def quant_breakdown(self, steps):
+        """Steps with events around every launch: median per quantise call."""
+        import statistics
+        for _ in range(steps):
+            self.step("all")
+        self.torch.cuda.synchronize()
+        qcalls = {}
+        for kind, label, nbytes, _, t in self.collect():
+            if kind == "quant":
+                qcalls.setdefault(label, [nbytes, []])[1].append(t)
+        q_ms = sum(statistics.median(ts) for _, ts in qcalls.values())
+        q_bytes = sum(nb for nb, _ in qcalls.values())
+        gbs = q_bytes / (q_ms * 1e-3) / 1e9
+        agg = {"GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "ms_per_step": round(q_ms, 4),
+               "avg_call_us": round(q_ms * 1e3 / len(qcalls), 2),
+               "bytes": "5 per element: amax read 2, cast read 2, row-major FP8 copy 1",
+               "timing": f"median per call over {steps} steps"}
+        per = {lb: {"us": round(statistics.median(ts) * 1e3, 1),
+                    "GB/s": round(nb / (statistics.median(ts) * 1e-3) / 1e9, 1)} for lb, (nb, ts) in qcalls.items()}
+        return agg, per
+
+
+def gemm_figures(timed, steps):
+    """GEMM aggregates from the timed steps' events: all GEMM launches, the
+    dominant kernel (the backward pair) and the forward, per launch and per
+    linear."""
+    def agg(kinds):
+        ms = sum(t for k, _, _, _, t in timed if k in kinds)
+        fl = sum(f for k, _, _, f, _ in timed if k in kinds)
+        n = sum(1 for k, *_ in timed if k in kinds)
+        return ms, fl, n
+    out = {}
+    for key, kinds in (("all", ("fwd", "pair")), ("pair", ("pair",)), ("fwd", ("fwd",))):
+        ms, fl, n = agg(kinds)
+        out[key] = {"TFLOP/s": round(fl / (ms * 1e-3) / 1e12, 1), "ms_per_step": round(ms / steps, 4),
+                    "launches_per_step": n // steps, "avg_launch_us": round(ms * 1e3 / n, 2),
+                    "flop_per_launch": fl // n}
+    per = {}
+    for kind, label, _, fl, t in timed:
+        if kind != "quant":
+            p = per.setdefault(label, [0.0, 0, fl])
+            p[0] += t
+            p[1] += 1
+    out["by_launch"] = {lb: {"us": round(t * 1e3 / n, 1), "TFLOP/s": round(fl / (t / n * 1e-3) / 1e12, 1)}
+                        for lb, (t, n, fl) in per.items()}
+    lt = {}
+    for kind, label, _, fl, t in timed:
+        if kind != "quant":
+            e = lt.setdefault(label.split(".")[0], [0.0, 0.0])
+            e[0] += t
+            e[1] += fl
+    out["by_linear"] = {n: {"us_per_step": round(t * 1e3 / steps, 1), "TFLOP/s": round(f / (t * 1e-3) / 1e12, 1)}
+                        for n, (t, f) in lt.items()}
+    return out
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import tensor_scaled_fp8_amd as tsf
+    from workloads import workload
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    tsf.load()
+    wl = workload(args.workload)
+
+    # Timing events are HIP events created once, without the system-scope
+    # fence on record (a fenced timing event writes back and invalidates the
+    # caches and measurably slows the kernels around it).
+    hip = HipEvents(torch.cuda.current_stream(dev).cuda_stream)
+    want_cpu = not args.no_cpu_baseline
+    layer = Layer(tsf, torch, np, wl, dev, hip, args.cpu_rows if want_cpu else 0, args.cpu_cols)
 
     if args.calibration_copy:
         n = args.calibration_copy
@@ -149,102 +251,62 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    for _ in range(args.warmup):
-        step(None)
-    hip.reserve(2 * 3 * len(lin) * args.steps + 2 * 6 * len(lin) * args.breakdown_steps)
-    # timed region: K whole steps; events bracket every GEMM launch
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step("gemm")
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms = (t1 - t0) * 1e3 / args.steps
+    # timed region: K whole steps bracketed by synchronisation; events
+    # bracket every GEMM launch
+    ms, timed = layer.timed(args.steps, args.warmup)
     flops = wl.flops_fwd_bwd()
     value = flops / (ms * 1e-3) / 1e12
-    timed = [(k, lb, b, f, hip.elapsed_ms(e0, e1)) for k, lb, b, f, e0, e1 in events]
-    # breakdown pass: the same steps with events around every launch (amax
-    # and cast figures; these events cost a little time, so this pass is
-    # kept out of the timed region)
-    events.clear()
-    brk, infer, fp8dw, o2, spec = [], None, None, None, None
+    g = gemm_figures(timed, args.steps)
+    dom = g["pair"]
+    traffic = gemm_traffic(os.path.join(args.traffic_dir, f"gemm_traffic_{wl.name}.json"), wl.name)
+    roofline = {"bound": "mfma", "achieved": dom["TFLOP/s"], "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(dom["TFLOP/s"] / PEAK_FP8_TFLOPS, 4), "traffic": traffic,
+                "kernel": f"{DOMINANT} (a linear's dgrad + wgrad in one launch, FP8 MFMA)",
+                "avg_launch_us": dom["avg_launch_us"], "flop_per_launch": dom["flop_per_launch"],
+                "note": "achieved = mean algorithmic FLOP per launch (4*M*K*N over the layer's linears) / "
+                        "mean launch duration (fence-free HIP events around each launch in the timed steps); "
+                        "the rocprofv3 average of the same kernel gives the same ratio"}
+    kernels = {"gemm": {"TFLOP/s": g["all"]["TFLOP/s"], "ms_per_step": g["all"]["ms_per_step"],
+                        "forward_gemm_nt": g["fwd"], "backward_pair": g["pair"]},
+               "gemm_by_launch": g["by_launch"], "gemm_by_linear": g["by_linear"]}
+    infer = fp8dw = o2 = spec = None
+    side = {}
     if not args.step_only:
-        for _ in range(args.breakdown_steps):
-            step("all")
-        torch.cuda.synchronize()
-        brk = [(k, lb, b, f, hip.elapsed_ms(e0, e1)) for k, lb, b, f, e0, e1 in events]
-        spec = spec_pass(tsf, torch, lin, margin, mu, hip, step, args.steps, flops, wl)
-        infer = inference_pass(tsf, torch, lin, margin, args.steps, args.warmup)
-        fp8dw = fp8_dw_pass(tsf, torch, lin, margin, mu, args.steps, args.warmup)
-        o2 = adam_pass(tsf, torch, lin, margin, mu, args.steps, args.warmup)
-
-    def aggregate(rows):
-        agg = {}
-        for kind, _, nbytes, fl, t in rows:
-            a = agg.setdefault(kind, {"ms": 0.0, "bytes": 0, "flops": 0, "n": 0})
-            a["ms"] += t
-            a["bytes"] += nbytes
-            a["flops"] += fl
-            a["n"] += 1
-        return agg
-
-    g = aggregate(timed)["gemm"]
-    gemm_tflops = g["flops"] / (g["ms"] * 1e-3) / 1e12
-    traffic = gemm_traffic(args.traffic)
-    roofline = {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": PEAK_FP8_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4), "traffic": traffic,
-                "kernel": "gemm_nt_kernel (forward) + gemm_pair_kernel (dgrad + wgrad), FP8 MFMA",
-                "avg_launch_us": round(g["ms"] * 1e3 / g["n"], 2)}
-    kernels = {}
-    # per call: the median over the breakdown steps (one slow call, e.g. a
-    # host hiccup between two events, would otherwise skew the sum)
-    import statistics
-    qcalls = {}
-    for kind, label, nbytes, _, t in brk:
-        if kind == "quant":
-            qcalls.setdefault(label, [nbytes, []])[1].append(t)
-    if qcalls:
-        q_ms = sum(statistics.median(ts) for _, ts in qcalls.values())
-        q_bytes = sum(nb for nb, _ in qcalls.values())
-        gbs = q_bytes / (q_ms * 1e-3) / 1e9
-        kernels["amax+cast"] = {"GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
-                                "ms_per_step": round(q_ms, 4), "avg_call_us": round(q_ms * 1e3 / len(qcalls), 2),
-                                "bytes": "5 per element: amax read 2, cast read 2, row-major FP8 copy 1",
-                                "timing": f"median per call over {args.breakdown_steps} steps"}
-    kernels["gemm"] = {"TFLOP/s": round(gemm_tflops, 1), "ms_per_step": round(g["ms"] / args.steps, 4)}
-    per = {}
-    for kind, label, _, fl, t in timed:
-        if kind == "gemm":
-            p = per.setdefault(label, [0.0, 0, fl])
-            p[0] += t
-            p[1] += 1
-    kernels["gemm_by_launch"] = {lb: {"us": round(t * 1e3 / n, 1), "TFLOP/s": round(fl / (t / n * 1e-3) / 1e12, 1)}
-                                 for lb, (t, n, fl) in per.items()}
-    # per tensor (warm, inside the step) and per linear (6*M*K*N over its three GEMMs)
-    kernels["amax+cast_by_tensor"] = {lb: {"us": round(statistics.median(ts) * 1e3, 1),
-                                           "GB/s": round(nb / (statistics.median(ts) * 1e-3) / 1e9, 1)}
-                                      for lb, (nb, ts) in qcalls.items()}
-    lt = {}
-    for kind, label, _, fl, t in timed:
-        if kind == "gemm":
-            e = lt.setdefault(label.split(".")[0], [0.0, 0.0])
-            e[0] += t
-            e[1] += fl
-    kernels["gemm_by_linear"] = {n: {"us_per_step": round(t * 1e3 / args.steps, 1),
-                                     "TFLOP/s": round(f / (t * 1e-3) / 1e12, 1)} for n, (t, f) in lt.items()}
-    if not args.step_only:
-        kernels["amax+cast_cold"] = quantize_cold(tsf, torch, lin, margin, mu, hip)
-    kernels["note"] = ("gemm: events in the timed region; amax+cast (fp8_quantize / fp8_quantize_batch: "
-                       f"amax pass + cast kernel): a separate pass of {args.breakdown_steps} steps with events "
-                       "around every call, median per call")
+        qa, qper = layer.quant_breakdown(args.breakdown_steps)
+        kernels["amax+cast"] = qa
+        kernels["amax+cast_by_tensor"] = qper
+        spec = spec_pass(tsf, torch, layer.lin, layer.margin, layer.mu, hip, layer.step, args.steps, flops, wl)
+        infer = inference_pass(tsf, torch, layer.lin, layer.margin, args.steps, args.warmup)
+        fp8dw = fp8_dw_pass(tsf, torch, layer.lin, layer.margin, layer.mu, args.steps, args.warmup)
+        o2 = adam_pass(tsf, torch, layer.lin, layer.margin, layer.mu, args.steps, args.warmup)
+        kernels["amax+cast_cold"] = quantize_cold(tsf, torch, layer.lin, layer.margin, layer.mu, hip)
+        kernels["note"] = ("gemm: events in the timed region; amax+cast (fp8_quantize / fp8_quantize_batch: "
+                           f"amax pass + cast kernel): a separate pass of {args.breakdown_steps} steps with "
+                           "events around every call, median per call")
+        for w in [int(x) for x in args.side_workloads.split(",") if x.strip()]:
+            if w == args.workload:
+                continue
+            other = Layer(tsf, torch, np, workload(w), dev, hip)
+            oms, otimed = other.timed(args.steps, args.warmup)
+            og = gemm_figures(otimed, args.steps)
+            oq, _ = other.quant_breakdown(args.breakdown_steps)
+            oflops = other.wl.flops_fwd_bwd()
+            side[other.wl.name] = {
+                "value": round(oflops / (oms * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "ms_per_step": round(oms, 4),
+                "tokens": other.lin[0]["L"].M, "linears": {L.name: [L.M, L.K, L.N] for L in other.wl.linears},
+                "gemm": {"TFLOP/s": og["all"]["TFLOP/s"], "frac": round(og["all"]["TFLOP/s"] / PEAK_FP8_TFLOPS, 4),
+                         "backward_pair": og["pair"]["TFLOP/s"], "forward_gemm_nt": og["fwd"]["TFLOP/s"]},
+                "amax+cast": oq}
+            del other
+            torch.cuda.synchronize()
 
     check = None
     if args.check:
-        check = sampled_check(lin, wl, margin, mu)
+        check = sampled_check(layer.lin, wl, layer.margin, layer.mu)
 
     cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, args.cpu_rows, args.cpu_cols)
+    if want_cpu:
+        cpu = cpu_baseline(wl, layer.sample, args.cpu_rows, args.cpu_cols)
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
@@ -253,17 +315,18 @@ def main():
         "dtype": "fp8 (E4M3 X/W, E5M2 dY; fp32 accumulate; bf16 in/out)", "data": "synthetic",
         "config": {"workload": wl.name, "tokens": wl.linears[0].M,
                    "linears": {L.name: [L.M, L.K, L.N] for L in wl.linears},
-                   "margin": margin, "mu_log2": mu, "flops_per_step": flops,
+                   "margin": layer.margin, "mu_log2": layer.mu, "flops_per_step": flops,
                    "quant_bytes_per_step": wl.quant_bytes()},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernels": kernels,
         "frac_fp8_peak_step": round(value / PEAK_FP8_TFLOPS, 4),
+        "other_workloads": side or None,
         "inference": infer,
         "fp8_weight_gradient": fp8dw,
         "o2_adam": o2,
         "quantize_speculative": spec,
-        "input_gen_s": round(t_gen, 1),
+        "input_gen_s": round(layer.gen_s, 1),
     }
     if check is not None:
         out["check"] = check
@@ -579,16 +642,19 @@ class HipEvents:
         return t.value
 
 
-def gemm_traffic(path):
-    """Measured HBM bytes per GEMM launch from a committed counter summary,
-    reported only while the GEMM code is the one the counters were taken on
-    (sha256 of gemm.hip without comments, recorded in the summary)."""
+def gemm_traffic(path, workload_name):
+    """Measured HBM bytes per launch of the dominant GEMM kernel from a
+    committed counter summary of this workload, reported only while the
+    GEMM code is the one the counters were taken on (sha256 of gemm.hip
+    without comments, recorded in the summary)."""
     from tensor_scaled_fp8_amd.profiling import gemm_code_sha256
     if not path or not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("gemm_code_sha256") != gemm_code_sha256():
+    if rec.get("gemm_code_sha256") != gemm_code_sha256() or rec.get("workload") != workload_name:
+        return None
+    if DOMINANT not in rec.get("kernel", ""):
         return None
     return round(rec["gemm_bytes_per_launch"])
 
@@ -626,14 +692,12 @@ def sampled_check(lin, wl, margin, mu):
     return {"mismatches": bad}
 
 
-def cpu_baseline(wl, rows, cols):
+def cpu_baseline(wl, sample, rows, cols):
     """The oracle, as it stands, on a bounded sample of the same layer: the
     first `rows` tokens and the first `cols` output features of every
-    linear (X [rows, K], W [K, cols], dY [rows, cols]): amax, bias, cast,
-    three fp64 GEMMs."""
-    import numpy as np
+    linear (X [rows, K], W [K, cols], dY [rows, cols], sliced from the
+    benchmark's own inputs): amax, bias, cast, three fp64 GEMMs."""
     import oracle
-    from workloads import linear_inputs
     try:
         from threadpoolctl import threadpool_info
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
@@ -641,11 +705,8 @@ def cpu_baseline(wl, rows, cols):
         cores = os.cpu_count() or 1
     flops = 0
     t = 0.0
-    for li, L in enumerate(wl.linears):
-        X, W, dY = linear_inputs(wl, li, rows_x=rows)
-        n = min(cols, L.N)
-        W = np.ascontiguousarray(W[:, :n])
-        dY = np.ascontiguousarray(dY[:, :n])
+    for (X, W, dY), L in zip(sample, wl.linears):
+        n = W.shape[1]
         t0 = time.perf_counter()
         oracle.linear_fwd_bwd(X, W, dY, wl.margin, wl.mu_log2, with_tolerance=False)
         t += time.perf_counter() - t0

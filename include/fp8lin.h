@@ -148,9 +148,12 @@ fp8_status fp8_amax_scale(const void* x_bf16, int64_t n, fp8_fmt fmt, int margin
                           fp8_scale_t* s_dev, hipStream_t stream);
 
 /*
- * The a2 rule on the host for one amax value (the same code the kernels
- * run). Returns the bias; *flags_out (nullable) receives FP8_FLAG_* bits.
- * Out-of-range margin/mu_log2 are clamped to +-1024.
+ * The a2 rule [AMAX bullet 2: bias = log2(format max / amax) with a
+ * configurable margin; FP8LM O1 Eq. 3: mu = 2^mu_log2 scales gradients] on
+ * the host for one amax value (the same code the kernels run). Returns the
+ * bias; *flags_out (nullable) receives FP8_FLAG_* bits. Out-of-range
+ * margin/mu_log2 are clamped to +-1024. Pure host function: no device
+ * memory, no stream, never fails.
  */
 int32_t fp8_bias_host(float amax, fp8_fmt fmt, int margin, int mu_log2, uint32_t* flags_out);
 
@@ -228,7 +231,8 @@ fp8_status fp8_scale_fixed(fp8_scale_t* s_dev, int32_t bias, hipStream_t stream)
 /*
  * a3 - cast (+ transpose) [AMAX bullets 3-4]: q = enc_fmt(x * 2^bias) with
  * round-to-nearest-even, saturation to +-max, subnormals kept, NaN ->
- * 0x7F|sign; bias from s_dev (device).
+ * 0x7F|sign (whatever the record's flags say, e.g. a fixed-bias record);
+ * bias from s_dev (device).
  *   x_bf16          device, [rows, cols] row-major bf16, 16-B aligned.
  *   out_rowwise     device, [rows, cols] u8, or NULL to skip.
  *   out_transposed  device, [cols, rows] u8, or NULL to skip.
@@ -377,15 +381,26 @@ typedef struct fp8_linear_ws {
 } fp8_linear_ws;
 
 /* Scratch bytes that let fp8_linear_fwd split its GEMM's last wave
- * (fp8_gemm_workspace_bytes with FP8_SPLIT_AUTO); 0 when it would not. */
+ * (fp8_gemm_workspace_bytes with FP8_SPLIT_AUTO) [AMAX bullet 3: the
+ * matmul on the scaled FP8 operands, whose FP32 partial sums the split
+ * keeps]; 0 when it would not. Negative sizes give 0. Host function, no
+ * device access. */
 size_t fp8_linear_scratch_bytes(int64_t M, int64_t K, int64_t N);
 
 /*
- * Forward of one linear, Y = X W: fp8_quantize of X and W (E4M3), then the
- * forward GEMM gemm(x8 ROWS, w8 COLS).
+ * Forward of one linear, Y = X W [AMAX "Proposed method" bullets 1-4:
+ * per-tensor amax of X and W, bias = log2(max / amax) - margin, scale and
+ * cast to E4M3, FP8 matmul, scaling undone after it; FP8LM O1 Eq. 3 for
+ * the bias rule's form]: fp8_quantize of X and W (E4M3), then the forward
+ * GEMM gemm(x8 ROWS, w8 COLS).
  *   X [M,K] bf16, W [K,N] bf16 (in x out), Y [M,N] bf16; device, 16-B aligned.
  *   M, K, N multiples of 16, every FP8 operand below 4 GiB. ws: host struct
- *   of device pointers (above).
+ *   of device pointers (above), read during the call only; the buffers it
+ *   names are the caller's and are written on the stream.
+ *   margin: |margin| <= 1024. Errors: FP8_ERR_INVALID (null / misaligned
+ *   pointer, negative size, bad margin, ws->sx == ws->sw),
+ *   FP8_ERR_UNSUPPORTED (a size not a multiple of 16 or too large),
+ *   FP8_ERR_HIP (launch failure); nothing is enqueued on an argument error.
  */
 fp8_status fp8_linear_fwd(const void* X, const void* W, int64_t M, int64_t K, int64_t N, int margin,
                           const fp8_linear_ws* ws, void* Y, hipStream_t stream);
@@ -393,11 +408,17 @@ fp8_status fp8_linear_fwd(const void* X, const void* W, int64_t M, int64_t K, in
  * ws->sw must be distinct records, else FP8_ERR_INVALID.) */
 
 /*
- * Backward of one linear: fp8_quantize of dY (E5M2, with mu = 2^mu_log2),
+ * Backward of one linear [AMAX "Proposed method" bullets 1-4: amax of dY,
+ * its bias with the margin, the E5 format for gradients, FP8 matmuls with
+ * the scaling undone after them; FP8LM O1 Eq. 3: the gradient's bias also
+ * takes log2 mu]: fp8_quantize of dY (E5M2, with mu = 2^mu_log2),
  * then dX = dY W^T = gemm(dy8 ROWS, w8 ROWS) and dW = X^T dY =
  * gemm(x8 COLS, dy8 COLS) from the FP8 copies the forward left in ws
  * (when both are asked for, as one fp8_gemm_pair launch).
  *   dY [M,N] bf16; dX [M,K] bf16 or NULL to skip; dW [K,N] bf16 or NULL to skip.
+ *   margin, mu_log2: |value| <= 1024. ws->sdy must differ from ws->sx and
+ *   ws->sw (FP8_ERR_INVALID otherwise: dY's quantise rewrites its record).
+ *   Other errors as for fp8_linear_fwd.
  */
 fp8_status fp8_linear_bwd(const void* dY, int64_t M, int64_t K, int64_t N, int margin, int mu_log2,
                           const fp8_linear_ws* ws, void* dX, void* dW, hipStream_t stream);
@@ -478,7 +499,8 @@ typedef enum fp8_scaling {
  * sw are what fp8_linear_fwd would produce from W.
  *   X [M,K] bf16, Y [M,N] bf16, w8t [N,K] u8, x8 [M,K] u8; device, 16-B
  *   aligned. M, K, N multiples of 16, x8 and w8t below 4 GiB.
- *   sw: read only. sx: written (AMAX) or read (FIXED).
+ *   sw: read only. sx: written (AMAX) or read (FIXED); sx == sw ->
+ *   FP8_ERR_INVALID. NaNs in X become NaN codes in either mode.
  */
 fp8_status fp8_linear_fwd_cached(const void* X, int64_t M, int64_t K, int64_t N, int margin,
                                  fp8_scaling x_scaling, const uint8_t* w8t, const fp8_scale_t* sw,

@@ -99,9 +99,12 @@ def saturated_count(bits, fmt: Fp8Format, bias: int) -> int:
         return int(np.count_nonzero(np.abs(np.ldexp(x, bias)) > fmt.max_finite))
 
 
-def cast(bits, fmt: Fp8Format, bias: int):
+def cast(bits, fmt: Fp8Format, bias: int, transposed: bool = True):
     """FP8 codes of t * 2^bias for a bf16 matrix [R, C]: (row-wise [R, C],
-    transposed [C, R]). The product is exact in float64."""
+    transposed [C, R], or None for it with transposed=False). The product
+    is exact in float64."""
     x = bf16_to_f64(bits)
     q = encode(np.ldexp(x, bias), fmt)
+    if not transposed:
+        return q, None
     return q, np.ascontiguousarray(q.T) if q.ndim == 2 else q

@@ -315,15 +315,54 @@ def fp8_linear_bwd(dY: torch.Tensor, ws: LinearWorkspace, margin: int = 0, mu_lo
     return dX, dW
 
 
+# Workspaces of the autograd path, reused across calls: free ones per
+# (M, K, N, device). A forward takes one (or builds one when none is free)
+# and holds it through a lease kept in the autograd context, since its FP8
+# copies and records are the backward's inputs; the lease gives it back
+# when the context is freed (after the backward, or when the graph is
+# dropped), so a training loop settles on one or two workspaces per shape
+# and allocates nothing more. Reuse is ordered by the stream: callers that
+# run forward and backward on different streams must order them.
+_WS_POOL = {}
+_WS_POOL_KEEP = 4            # free workspaces kept per shape
+
+
+class _Lease:
+    __slots__ = ("key", "ws")
+
+    def __init__(self, key, ws):
+        self.key, self.ws = key, ws
+
+    def __del__(self):
+        try:
+            free = _WS_POOL.setdefault(self.key, [])
+            if len(free) < _WS_POOL_KEEP:
+                free.append(self.ws)
+        except Exception:     # interpreter shutdown: the pool may be gone
+            pass
+
+
+def _lease_workspace(M: int, K: int, N: int, device) -> _Lease:
+    key = (M, K, N, str(torch.device(device)))
+    free = _WS_POOL.get(key)
+    ws = free.pop() if free else LinearWorkspace(M, K, N, device)
+    return _Lease(key, ws)
+
+
+def release_workspaces() -> None:
+    """Drop the free workspaces the autograd path keeps for reuse."""
+    _WS_POOL.clear()
+
+
 class _FP8LinearFn(torch.autograd.Function):
     @staticmethod
     def forward(ctx, X, W, margin, mu_log2):
         Xc, Wc = X.contiguous(), W.contiguous()
         lead = Xc.shape[:-1]
         X2 = Xc.reshape(-1, Xc.shape[-1])
-        ws = LinearWorkspace(X2.shape[0], X2.shape[1], Wc.shape[1], X.device)
-        Y = fp8_linear_fwd(X2, Wc, ws, margin)
-        ctx.ws, ctx.margin, ctx.mu_log2, ctx.lead = ws, margin, mu_log2, lead
+        lease = _lease_workspace(X2.shape[0], X2.shape[1], Wc.shape[1], X.device)
+        Y = fp8_linear_fwd(X2, Wc, lease.ws, margin)
+        ctx.lease, ctx.margin, ctx.mu_log2, ctx.lead = lease, margin, mu_log2, lead
         return Y.reshape(*lead, Wc.shape[1])
 
     @staticmethod
@@ -331,7 +370,7 @@ class _FP8LinearFn(torch.autograd.Function):
         dY2 = dY.contiguous().reshape(-1, dY.shape[-1])
         if dY2.dtype != torch.bfloat16:
             dY2 = dY2.to(torch.bfloat16)
-        dX, dW = fp8_linear_bwd(dY2, ctx.ws, ctx.margin, ctx.mu_log2,
+        dX, dW = fp8_linear_bwd(dY2, ctx.lease.ws, ctx.margin, ctx.mu_log2,
                                 need_dx=ctx.needs_input_grad[0], need_dw=ctx.needs_input_grad[1])
         if dX is not None:
             dX = dX.reshape(*ctx.lead, dX.shape[-1])

@@ -251,6 +251,8 @@ fp8_status fp8_linear_bwd(const void* dY, int64_t M, int64_t K, int64_t N, int m
   if (st != FP8_OK) return st;
   if ((M * N > 0 && (!dY || !aligned16(dY))) || (dX && !aligned16(dX)) || (dW && !aligned16(dW)))
     return FP8_ERR_INVALID;
+  // dY's quantise rewrites sdy, which the GEMMs read beside sx and sw
+  if (ws->sdy == ws->sx || ws->sdy == ws->sw) return FP8_ERR_INVALID;
   hipError_t e;
   if ((e = launch_quantize(dY, M, N, FP8_E5M2, margin, mu_log2, ws->sdy, ws->dy8, ws->dy8t,
                            stream)) != hipSuccess)
@@ -273,6 +275,7 @@ fp8_status fp8_linear_fwd_cached(const void* X, int64_t M, int64_t K, int64_t N,
   if (M < 0 || K < 0 || N < 0 || !int_ok(margin)) return FP8_ERR_INVALID;
   if (x_scaling != FP8_SCALING_AMAX && x_scaling != FP8_SCALING_FIXED) return FP8_ERR_INVALID;
   if (!sw || !aligned16(sw) || !sx || !aligned16(sx)) return FP8_ERR_INVALID;
+  if (sx == sw) return FP8_ERR_INVALID;  // X's quantise would rewrite the weight's record
   if (M % 16 || K % 16 || N % 16 || M >= kMaxDim || K >= kMaxDim || N >= kMaxDim || !gemm_fits(M, N, K))
     return FP8_ERR_UNSUPPORTED;
   if ((M * K > 0 && (!X || !aligned16(X) || !x8 || !aligned16(x8))) ||

@@ -6,8 +6,10 @@
 // activations, E5M2 for gradients). The product is exact (a power of two);
 // it is clamped to +-max (saturation; inf -> max) and converted by the
 // hardware FP8 converter, which rounds to nearest even and keeps
-// subnormals. NaN inputs (only possible when the tensor's record carries
-// FP8_FLAG_NONFINITE) are patched to 0x7F|sign afterwards.
+// subnormals. NaN inputs are patched to 0x7F|sign afterwards: with a
+// derived scale only where the record's FP8_FLAG_NONFINITE says the tensor
+// holds one; with a published record (e.g. a fixed bias, whose record says
+// nothing about the tensor) wherever a thread's patch holds one.
 //
 // Inputs are read with nontemporal loads (streamed past the caches).
 // Tiling: one 256-thread block per 128 x 128 tile. Each thread loads an
@@ -144,8 +146,10 @@ __device__ __forceinline__ void cast_tile(const uint16_t* __restrict__ x, int64_
       s->epoch = word >> 16;  // this call's maximum is consumed
     }
   } else {
+    // a published record need not describe this tensor (fp8_scale_fixed
+    // writes no flags): NaNs are looked for in each patch below
     scale = s->scale;
-    nonfinite = (s->flags & FP8_FLAG_NONFINITE) != 0u;
+    nonfinite = false;
   }
   const int64_t rr = r0 + 8 * rg, cx = c0 + 8 * cc;
   const bool ok = rr < rows && cx < cols;  // rows, cols are multiples of 16
@@ -172,6 +176,18 @@ __device__ __forceinline__ void cast_tile(const uint16_t* __restrict__ x, int64_
     for (int i = 0; i < 8; ++i) {
       lo[i] = cvt4<FMT>(v[i].x, v[i].y, scale);
       hi[i] = cvt4<FMT>(v[i].z, v[i].w, scale);
+    }
+    if constexpr (!DERIVE) {
+      // any NaN (magnitude bits above 0x7F80) in this thread's patch
+      u16x2 m = {0, 0};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, (uint32_t)(v[i].x & 0x7FFF7FFFu)));
+        m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, (uint32_t)(v[i].y & 0x7FFF7FFFu)));
+        m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, (uint32_t)(v[i].z & 0x7FFF7FFFu)));
+        m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, (uint32_t)(v[i].w & 0x7FFF7FFFu)));
+      }
+      nonfinite = (m.x > m.y ? m.x : m.y) > 0x7F80u;
     }
     if (nonfinite) {
 #pragma unroll

@@ -65,7 +65,8 @@ def _short(name: str) -> str:
     return base.split("::")[-1][:60]
 
 
-def stats_markdown(d: str, title: str, command: str) -> str:
+def stats_markdown(d: str, title: str, command: str, dominant: str = "", flop_per_launch: float = 0.0,
+                   peak_tflops: float = 5000.0) -> str:
     st = kernel_stats(d)
     tot = sum(v["total_us"] for v in st.values())
     lines = [f"# {title}", "", "Command:", "", "```", command, "```", "",
@@ -73,6 +74,15 @@ def stats_markdown(d: str, title: str, command: str) -> str:
     for k, v in sorted(st.items(), key=lambda kv: -kv[1]["total_us"]):
         lines.append(f"| `{_short(k)}` | {v['count']} | {v['total_us']:.1f} | {v['avg_us']:.2f} | "
                      f"{100 * v['total_us'] / tot:.1f}% |")
+    if dominant and flop_per_launch:
+        hits = [v for k, v in st.items() if dominant in k]
+        if hits:
+            calls = sum(v["count"] for v in hits)
+            avg = sum(v["total_us"] for v in hits) / calls
+            tf = flop_per_launch / (avg * 1e-6) / 1e12
+            lines += ["", f"Roofline of the dominant kernel `{dominant}`: {flop_per_launch:.6g} algorithmic "
+                      f"FLOP per launch (mean over the step's launches) / {avg:.2f} us average duration = "
+                      f"{tf:.1f} TFLOP/s, {tf / peak_tflops:.4f} of {peak_tflops:.0f} TFLOP/s."]
     return "\n".join(lines) + "\n"
 
 
@@ -88,7 +98,7 @@ def _pmc(d: str, counter: str) -> dict:
     return {k: (names[k], v) for k, v in per.items()}
 
 
-def traffic(fetch_dir: str, write_dir: str, kernel: str, copy_bytes: int) -> dict:
+def traffic(fetch_dir: str, write_dir: str, kernel: str, copy_bytes: int, workload: str = "") -> dict:
     out = {}
     for key, d, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
         per = _pmc(d, counter)
@@ -105,6 +115,7 @@ def traffic(fetch_dir: str, write_dir: str, kernel: str, copy_bytes: int) -> dic
         out[f"{key}_dispatches"] = len(vals)
     out["gemm_bytes_per_launch"] = out["fetch_bytes_per_dispatch"] + out["write_bytes_per_dispatch"]
     out["kernel"] = kernel
+    out["workload"] = workload
     out["copy_bytes"] = copy_bytes
     out["gemm_code_sha256"] = gemm_code_sha256()
     return out
@@ -138,7 +149,8 @@ def _copy_factor(rows: dict, counter: str, copy_bytes: int) -> float:
     return copy_bytes / (max(copies) * 1024.0)
 
 
-def quant_traffic_markdown(fetch_dir: str, write_dir: str, copy_bytes: int, command: str) -> str:
+def quant_traffic_markdown(fetch_dir: str, write_dir: str, copy_bytes: int, command: str,
+                           layer: str = "GPT-175B-style layer") -> str:
     fe, wr = _pmc_rows(fetch_dir), _pmc_rows(write_dir)
     ff, wf = _copy_factor(fe, "FETCH_SIZE", copy_bytes), _copy_factor(wr, "WRITE_SIZE", copy_bytes)
     fk, wk = sorted(fe, key=int), sorted(wr, key=int)
@@ -165,7 +177,7 @@ def quant_traffic_markdown(fetch_dir: str, write_dir: str, copy_bytes: int, comm
                 groups[(key, nxt["grid"] * 64)].append((fb, wb))
             else:
                 groups[(key, None)].append((fb, wb))
-    lines = ["# HBM traffic of the quantise kernels (amax and cast), GPT-7B-style layer", "",
+    lines = [f"# HBM traffic of the quantise kernels (amax and cast), {layer}", "",
              "Commands (FETCH_SIZE and WRITE_SIZE in separate runs; counters scaled by a plain "
              f"{copy_bytes}-byte device copy in the same run: fetch x{ff:.3f}, write x{wf:.3f}):", "",
              "```", command, "```", "",
@@ -187,7 +199,7 @@ def quant_traffic_markdown(fetch_dir: str, write_dir: str, copy_bytes: int, comm
     return "\n".join(lines) + "\n"
 
 
-def mfma_markdown(d: str, command: str) -> str:
+def mfma_markdown(d: str, command: str, layer: str = "GPT-175B-style layer") -> str:
     rows = _pmc_rows(d)
     groups = defaultdict(list)
     for e in rows.values():
@@ -196,7 +208,7 @@ def mfma_markdown(d: str, command: str) -> str:
             continue
         tmpl = e["name"][e["name"].index(key):].split(">")[0] + ">"
         groups[(tmpl, e["grid"] // 256)].append(e)
-    lines = ["# FP8 MFMA utilisation and shader clock of the GEMM kernel, GPT-7B-style layer", "",
+    lines = [f"# FP8 MFMA utilisation and shader clock of the GEMM kernel, {layer}", "",
              "Command:", "", "```", command, "```", "",
              "flops = 512 x (SQ_INSTS_VALU_MFMA_MOPS_F8 + SQ_INSTS_VALU_MFMA_MOPS_F6F4); MFMA cycles = "
              "SQ_VALU_MFMA_BUSY_CYCLES per SIMD (1024 SIMDs), which the hardware counts as 64 per "
@@ -230,12 +242,16 @@ def main():
     a.add_argument("dir")
     a.add_argument("--title", default="rocprofv3 kernel statistics")
     a.add_argument("--command", default="")
+    a.add_argument("--dominant", default="", help="kernel name part of the dominant kernel")
+    a.add_argument("--flop-per-launch", type=float, default=0.0,
+                   help="its algorithmic FLOP per launch (bench.py prints it as roofline.flop_per_launch)")
     a.add_argument("--out")
     b = sub.add_parser("traffic")
     b.add_argument("--fetch", required=True)
     b.add_argument("--write", required=True)
-    b.add_argument("--kernel", default="gemm_nt_kernel,gemm_pair_kernel",
+    b.add_argument("--kernel", default="gemm_pair_kernel",
                    help="comma-separated kernel name parts; dispatches of any of them are averaged")
+    b.add_argument("--workload", default="", help="workload name recorded with the figures")
     b.add_argument("--copy-bytes", type=int, required=True)
     b.add_argument("--command", default="")
     b.add_argument("--out")
@@ -244,20 +260,22 @@ def main():
     c.add_argument("--write", required=True)
     c.add_argument("--copy-bytes", type=int, required=True)
     c.add_argument("--command", default="")
+    c.add_argument("--layer", default="GPT-175B-style layer")
     c.add_argument("--out")
     m = sub.add_parser("mfma")
     m.add_argument("dir")
     m.add_argument("--command", default="")
+    m.add_argument("--layer", default="GPT-175B-style layer")
     m.add_argument("--out")
     args = ap.parse_args()
     if args.cmd == "stats":
-        text = stats_markdown(args.dir, args.title, args.command)
+        text = stats_markdown(args.dir, args.title, args.command, args.dominant, args.flop_per_launch)
     elif args.cmd == "quant-traffic":
-        text = quant_traffic_markdown(args.fetch, args.write, args.copy_bytes, args.command)
+        text = quant_traffic_markdown(args.fetch, args.write, args.copy_bytes, args.command, args.layer)
     elif args.cmd == "mfma":
-        text = mfma_markdown(args.dir, args.command)
+        text = mfma_markdown(args.dir, args.command, args.layer)
     else:
-        t = traffic(args.fetch, args.write, args.kernel, args.copy_bytes)
+        t = traffic(args.fetch, args.write, args.kernel, args.copy_bytes, args.workload)
         if args.command:
             t["command"] = args.command
         text = json.dumps(t, indent=1) + "\n"

@@ -177,6 +177,10 @@ def test_argument_validation_without_launch():
     # the forward's scratch is optional, but aligned when given
     ws_scr = _lib.LinearWs(ok, None, ok, None, ok, None, ok, ok + 64, ok + 128, ok + 8, 1 << 20)
     assert lib.fp8_linear_fwd(_vp(ok), _vp(ok), 16, 16, 16, 0, ctypes.byref(ws_scr), _vp(ok), None) == INV
+    # the backward's dY record must differ from X's and W's (its quantise rewrites it)
+    for sdy in (ok, ok + 64):
+        ws_dy = _lib.LinearWs(ok, None, ok, None, ok, None, ok, ok + 64, sdy)
+        assert lib.fp8_linear_bwd(_vp(ok), 16, 16, 16, 0, 0, ctypes.byref(ws_dy), _vp(ok), _vp(ok), None) == INV
     ws_nox = _lib.LinearWs(None, None, ok, None, ok, None, ok, ok, ok)
     assert lib.fp8_linear_fwd(_vp(ok), _vp(ok), 16, 16, 16, 0, ctypes.byref(ws_nox), _vp(ok), None) == INV
     # fixed bias: only [-126, 126]
@@ -188,7 +192,7 @@ def test_argument_validation_without_launch():
     c = lib.fp8_linear_fwd_cached
     args = lambda **kw: [kw.get(k, d) for k, d in (
         ("X", _vp(ok)), ("M", 16), ("K", 16), ("N", 16), ("margin", 0), ("mode", 0), ("w8t", _vp(ok)),
-        ("sw", _vp(ok)), ("x8", _vp(ok)), ("sx", _vp(ok)), ("Y", _vp(ok)), ("st", None))]
+        ("sw", _vp(ok)), ("x8", _vp(ok)), ("sx", _vp(ok + 64)), ("Y", _vp(ok)), ("st", None))]
     assert c(*args(mode=2)) == INV
     assert c(*args(K=24)) == UNS
     assert c(*args(sw=None)) == INV
@@ -197,6 +201,8 @@ def test_argument_validation_without_launch():
     assert c(*args(w8t=None)) == INV
     assert c(*args(Y=_vp(ok + 2))) == INV
     assert c(*args(margin=-5000)) == INV
+    assert c(*args(sx=_vp(ok))) == INV                  # X's record shared with W's
+    assert c(*args(sx=_vp(ok), mode=1)) == INV
     # FP8 weight gradient
     wg = lib.fp8_wgrad_fp8
     wargs = lambda **kw: [kw.get(k, d) for k, d in (

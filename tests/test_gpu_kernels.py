@@ -308,6 +308,37 @@ def test_autograd_linear_module():
     assert rel < 0.08
 
 
+def test_autograd_linear_reuses_workspace_and_matches_oracle():
+    """Training-loop use of the drop-in module: after the first step the
+    forward takes a free workspace from the pool (no new device buffers),
+    and every step's Y, dX and dW are the oracle's within the GEMM
+    tolerance, with the FP8 copies of that step's inputs."""
+    tsf.release_workspaces()
+    M, K, N, margin, mu = 128, 256, 384, 1, 2
+    lin = tsf.Linear(K, N, margin=margin, mu_log2=mu, device="cuda")
+    wb = bf16_bits(lin.weight.detach())
+    seen = []
+    for step in range(4):
+        xb = draw_normal_bf16(900 + step, (M, K), 1.0)
+        dyb = draw_normal_bf16(950 + step, (M, N), 1e-5)
+        x = to_dev_bf16(xb).requires_grad_(True)
+        lin.weight.grad = None
+        y = lin(x)
+        ws = y.grad_fn.lease.ws
+        seen.append(tuple(t.data_ptr() for t in (ws.x8, ws.w8, ws.dy8, ws.scales)))
+        y.backward(to_dev_bf16(dyb))
+        torch.cuda.synchronize()
+        ref = oracle.linear_fwd_bwd(xb, wb, dyb, margin, mu)
+        for key, t in (("Y", y), ("dX", x.grad), ("dW", lin.weight.grad)):
+            bits, c64, tol = ref[key]
+            err = np.abs(oracle.bf16_to_f64(bf16_bits(t)) - oracle.bf16_to_f64(bits))
+            assert np.all(err <= tol), (step, key, float((err / tol).max()))
+        del y, x
+    # steps 1.. reuse the workspace step 0 built (its graph freed before the next forward)
+    assert len(set(seen)) == 1, seen
+    tsf.release_workspaces()
+
+
 # ---------------------------------------------------------------- a1+a2+a3 fused
 @pytest.mark.parametrize("shape", [(16, 16), (144, 272), (528, 1040), (2064, 784)])
 @pytest.mark.parametrize("fmt_id,margin,mu", [(0, 0, 0), (1, 1, -2), (1, 0, 3), (0, 2, 0)])

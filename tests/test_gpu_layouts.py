@@ -113,3 +113,23 @@ def test_layouts_operand_of_2gib():
     bits, _, tol = oracle.gemm_nt(a.cpu().numpy(), E4M3, 3, b_sample, E4M3, 4)
     got = oracle.bf16_to_f64(bf16_bits(out[:, cols]))
     assert np.all(np.abs(got - oracle.bf16_to_f64(bits)) <= tol)
+
+
+@pytest.mark.parametrize("M,N,R", [(2320, 784, 528), (2576, 1808, 1040), (4112, 528, 144)])
+@pytest.mark.parametrize("fa,fb", [(0, 0), (1, 0), (0, 1)])
+def test_grouped_tile_order_every_element(M, N, R, fa, fb):
+    """Shapes with more than 8 tile rows, so the tile order's 8-row raster
+    groups engage and the last group is ragged (2320 = 9 tiles + 16 rows:
+    groups of 8 and 2 tile rows; 2576: 11 tile rows; 4112: 17), with ragged
+    tile columns and reductions; the tile count (40, 88, 51) is a multiple
+    of 8 in the first two (the XCD remap engages) and not in the third.
+    Every output element against the oracle, in every operand layout."""
+    A, B = _operands(M, N, R, fa, fb, 5 * M + N + R + fa + 2 * fb)
+    bits, _, tol = oracle.gemm_nt(A, FMT[fa], 6, B, FMT[fb], 11)
+    want = oracle.bf16_to_f64(bits)
+    for la, lb in [("rows", "rows")] + LAYOUTS:
+        out = _run(A, fa, 6, B, fb, 11, la, lb)
+        torch.cuda.synchronize()
+        err = np.abs(oracle.bf16_to_f64(bf16_bits(out)) - want)
+        bad = ~(err <= tol)
+        assert not bad.any(), (la, lb, int(bad.sum()), np.argwhere(bad)[:4].tolist())

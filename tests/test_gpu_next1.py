@@ -156,3 +156,61 @@ def test_cached_forward_full_size_gpt7b_up():
     r = tsf.read_scale(sx)
     want = oracle.scale_record(X, E4M3)
     assert (r["bias"], r["flags"], f32_bits(r["amax"])) == (want["bias"], want["flags"], f32_bits(want["amax"]))
+
+
+ALL_BF16 = np.arange(65536, dtype=np.uint32).astype(np.uint16).reshape(256, 256)
+
+
+@pytest.mark.parametrize("fmt_id", [0, 1])
+def test_cscale_cast_all_bf16_patterns_with_nans(fmt_id):
+    """A fixed-bias record carries no flags (the tensor is never inspected),
+    yet NaN inputs must still become the NaN code: every bf16 pattern (NaNs,
+    infs, subnormals, +-0) through fp8_scale_fixed + fp8_cast, row-wise and
+    transposed, against the oracle's encoder."""
+    fmt, name = (E4M3, E5M2)[fmt_id], ("e4m3", "e5m2")[fmt_id]
+    x = to_dev_bf16(ALL_BF16)
+    s = tsf.new_scale(1)[0]
+    for b in (-126, -1, 0, 1, 6, 29, 126):
+        tsf.fp8_scale_fixed(s, b)
+        rw, tr = tsf.fp8_cast(x, name, s)
+        want, want_t = oracle.cast(ALL_BF16, fmt, b)
+        got = u8(rw)
+        bad = np.argwhere(got != want)
+        assert bad.size == 0, (b, [(hex(ALL_BF16[i, j]), hex(got[i, j]), hex(want[i, j])) for i, j in bad[:8]])
+        assert np.array_equal(u8(tr), want_t), b
+
+
+@pytest.mark.parametrize("mode", ["fixed", "amax"])
+def test_cached_forward_nan_in_x(mode):
+    """fp8_linear_fwd_cached with NaNs in X: the x8 bytes equal the oracle's
+    cast (NaN codes where X is NaN), in the fixed-bias mode as in the amax
+    mode (whose record flags the NaN and takes bias 0); output rows that
+    met no NaN stay within the GEMM tolerance, rows that did are NaN."""
+    M, K, N = 272, 400, 528
+    g = np.random.Generator(np.random.PCG64(77))
+    xb = oracle.f64_to_bf16_rne(g.standard_normal((M, K)))
+    nan_rows = [3, 100, 271]
+    for r, c, v in ((3, 5, 0x7FC0), (100, 399, 0xFFC1), (271, 0, 0x7F81)):
+        xb[r, c] = v
+    wb = oracle.f64_to_bf16_rne(g.standard_normal((K, N)) * 0.02)
+    X, W = to_dev_bf16(xb), to_dev_bf16(wb)
+    w8t, sw = tsf.prepare_weight(W, fixed_bias=11)
+    sx = tsf.new_scale(1)[0]
+    if mode == "fixed":
+        tsf.fp8_scale_fixed(sx, 0)
+    x8 = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+    Y = tsf.fp8_linear_fwd_cached(X, w8t, sw, x8, sx, x_scaling=mode)
+    bx = 0                                      # fixed 0; the amax rule gives 0 with FLAG_NONFINITE
+    if mode == "amax":
+        r = tsf.read_scale(sx)
+        assert (r["bias"], r["flags"] & oracle.FLAG_NONFINITE) == (0, oracle.FLAG_NONFINITE)
+    want8 = oracle.cast(xb, E4M3, bx)[0]
+    assert np.array_equal(u8(x8), want8)
+    assert all((want8[r] & 0x7F == 0x7F).any() for r in nan_rows)
+    y = oracle.bf16_to_f64(bf16_bits(Y))
+    ok_rows = np.setdiff1d(np.arange(M), nan_rows)
+    assert np.isnan(y[nan_rows]).all()
+    qb = oracle.cast(np.ascontiguousarray(wb.T), E4M3, 11)[0]
+    want, _, tol = oracle.gemm_nt(want8[ok_rows], E4M3, bx, qb, E4M3, 11)
+    err = np.abs(y[ok_rows] - oracle.bf16_to_f64(want))
+    assert (err <= tol).all()

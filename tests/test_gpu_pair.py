@@ -138,3 +138,26 @@ def test_pair_full_size_gpt7b_bit_identical(name, M, K, N):
                                   np.ascontiguousarray(dy_h.T), E5M2, 23)
     err = np.abs(oracle.bf16_to_f64(bf16_bits(dW[-16:])) - oracle.bf16_to_f64(bits))
     assert not np.any(~(err <= tol)), (name, float(np.max(err / tol)))
+
+
+@pytest.mark.parametrize("M,K,N", [(2320, 784, 528), (528, 2576, 272)])
+def test_pair_grouped_tile_order_every_element(M, K, N):
+    """The backward pair on shapes whose dgrad or wgrad has more than 8 tile
+    rows (ragged last raster group, ragged tiles and reductions): every
+    element of both outputs against the oracle."""
+    g = np.random.Generator(np.random.PCG64(M + 7 * K + 13 * N))
+    x = oracle.encode(g.standard_normal((M, K)) * 40, E4M3)
+    w = oracle.encode(g.standard_normal((K, N)) * 40, E4M3)
+    dy = oracle.encode(g.standard_normal((M, N)) * 1000, E5M2)
+    sx, sw, sdy = scale_record(6), scale_record(11), scale_record(23)
+    xd, wd, dyd = (torch.from_numpy(a).cuda() for a in (x, w, dy))
+    dgrad = dict(a=dyd, fa="e5m2", sa=sdy, b=wd, fb="e4m3", sb=sw)
+    wgrad = dict(a=xd, fa="e4m3", sa=sx, b=dyd, fb="e5m2", sb=sdy, a_layout="cols", b_layout="cols")
+    dX, dW = tsf.fp8_gemm_pair(dgrad, wgrad)
+    torch.cuda.synchronize()
+    for out, A, fa, ba, B, fb, bb in ((dX, dy, E5M2, 23, w, E4M3, 11),
+                                      (dW, np.ascontiguousarray(x.T), E4M3, 6, np.ascontiguousarray(dy.T), E5M2, 23)):
+        bits, _, tol = oracle.gemm_nt(A, fa, ba, B, fb, bb)
+        err = np.abs(oracle.bf16_to_f64(bf16_bits(out)) - oracle.bf16_to_f64(bits))
+        bad = ~(err <= tol)
+        assert not bad.any(), (out.shape, int(bad.sum()), np.argwhere(bad)[:4].tolist())
