@@ -13,14 +13,17 @@ Per linear, against the oracle on the same seeded inputs:
       - GPT-7B-style and GPT-175B-style layers (the benchmark's workloads):
         every output element, with the workspace exactly as the benchmark
         sets it up (row-major copies only);
-      - GPT-125M MLP up: every element, transposed copies written too;
-      - GPT-13B-style and Llama-2-70B-style layers: the first and the last
-        256-row band and a 256-column band of every output (whole rows and
-        whole columns of tiles, so every tile-row and tile-column index of
-        the tile order is reached), with transposed copies written too and
+      - GPT-125M MLP up, GPT-13B-style and Llama-2-70B-style layers: every
+        output element as well, with the transposed copies written too and
         checked equal to the row-major ones transposed (a property at any
         size).
+A workload left out of EVERY is checked on the first and the last 256-row
+band and a 256-column band of every output (whole rows and whole columns of
+tiles, so every tile-row and tile-column index of the tile order is
+reached).
 """
+import time
+
 import numpy as np
 import pytest
 import torch
@@ -34,7 +37,7 @@ from workloads import WORKLOADS, linear_inputs
 
 pytestmark = pytest.mark.gpu
 
-EVERY = (1, 2, 4)          # workloads checked on every output element
+EVERY = (1, 2, 3, 4, 5)    # workloads checked on every output element
 CASES = [(w, li) for w in sorted(WORKLOADS) for li in range(len(WORKLOADS[w].linears))]
 
 
@@ -55,6 +58,7 @@ def test_full_size_linear(wl_idx, li):
     L = wl.linears[li]
     every = wl_idx in EVERY
     print(f"\n[full-size] {wl.name} {L.name} M={L.M} K={L.K} N={L.N} every_element={every}", flush=True)
+    t0 = time.perf_counter()
     X, W, dY = linear_inputs(wl, li)
     transposed = wl_idx not in (2, 4)
     ws = tsf.LinearWorkspace(L.M, L.K, L.N, transposed=transposed)
@@ -90,9 +94,13 @@ def test_full_size_linear(wl_idx, li):
         c0 = int(g.integers(0, (N + T - 1) // T)) * T
         return dict(row_bands=[(0, min(T, M)), (last, M)], col_bands=[(c0, min(N, c0 + T))])
 
+    print(f"[full-size] records and FP8 bytes bit-exact ({time.perf_counter() - t0:.1f} s)", flush=True)
     # Y = X W: A = x8 [M, K], B = w8 [K, N]
-    check_gemm(Y, xd, wd, bx, bw, f"{wl.name}.{L.name} Y", **bands(L.M, L.N))
+    n = check_gemm(Y, xd, wd, bx, bw, f"{wl.name}.{L.name} Y", **bands(L.M, L.N))
+    print(f"[full-size] Y ok ({n} checked with their sums, {time.perf_counter() - t0:.1f} s)", flush=True)
     # dX = dY W^T: A = dy8 [M, N], B = w8^T [N, K]
-    check_gemm(dX, dyd, wd.T, bdy, bw, f"{wl.name}.{L.name} dX", **bands(L.M, L.K))
+    n = check_gemm(dX, dyd, wd.T, bdy, bw, f"{wl.name}.{L.name} dX", **bands(L.M, L.K))
+    print(f"[full-size] dX ok ({n} checked with their sums, {time.perf_counter() - t0:.1f} s)", flush=True)
     # dW = X^T dY: A = x8^T [K, M], B = dy8 [M, N]
-    check_gemm(dW, xd.T, dyd, bx, bdy, f"{wl.name}.{L.name} dW", **bands(L.K, L.N))
+    n = check_gemm(dW, xd.T, dyd, bx, bdy, f"{wl.name}.{L.name} dW", **bands(L.K, L.N))
+    print(f"[full-size] dW ok ({n} checked with their sums, {time.perf_counter() - t0:.1f} s)", flush=True)
