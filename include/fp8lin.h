@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define FP8LIN_ABI_VERSION 10
+#define FP8LIN_ABI_VERSION 11
 
 typedef enum fp8_fmt {
   FP8_E4M3 = 0, /* OCP E4M3FN: weights and activations [AMAX bullet 4] */
@@ -321,6 +321,31 @@ fp8_status fp8_gemm_ws(const uint8_t* A, fp8_fmt fa, fp8_layout la, const fp8_sc
                        fp8_fmt fb, fp8_layout lb, const fp8_scale_t* sb, int64_t M, int64_t N, int64_t R,
                        void* C_bf16, fp8_split split, void* workspace, size_t workspace_bytes,
                        hipStream_t stream);
+
+/* Bytes of the device scratch fp8_gemm_noalloc uses (the tail split's FP32
+ * partials of at most 128 tiles: 64 MiB, held per device from library load
+ * to process end). */
+#define FP8_NOALLOC_SCRATCH_BYTES ((size_t)128 * 2 * 65536 * 4)
+
+/*
+ * fp8_gemm_ws without a caller workspace, for callers that cannot allocate
+ * device memory or bring a workspace: code being captured into a HIP graph,
+ * tight serving loops, harnesses that forbid hipMalloc. Same arguments,
+ * checks and result as fp8_gemm_ws (same kernels: bit-identical output),
+ * with the tail split's partials in a scratch array the library's code
+ * object holds on each device (FP8_NOALLOC_SCRATCH_BYTES). The call
+ * allocates nothing; its first call on a device looks up that device's
+ * scratch address (the current device must be the stream's). A split
+ * that would need more than the scratch holds -> FP8_ERR_UNSUPPORTED
+ * (nothing enqueued; with at most 256 CUs every split fits). Every call
+ * on a device shares that device's scratch: calls that may overlap on one
+ * GPU (different streams, no event between them) race and must be
+ * serialised by the caller. The scratch is written before it is read
+ * within a call, so nothing needs clearing between calls.
+ */
+fp8_status fp8_gemm_noalloc(const uint8_t* A, fp8_fmt fa, fp8_layout la, const fp8_scale_t* sa, const uint8_t* B,
+                            fp8_fmt fb, fp8_layout lb, const fp8_scale_t* sb, int64_t M, int64_t N, int64_t R,
+                            void* C_bf16, fp8_split split, hipStream_t stream);
 
 /* The arguments of one fp8_gemm call. */
 typedef struct fp8_gemm_args {

@@ -239,6 +239,20 @@ def fp8_gemm(a: torch.Tensor, fa, sa: torch.Tensor, b: torch.Tensor, fb, sb: tor
 SPLITS = {"auto": FP8_SPLIT_AUTO, "never": FP8_SPLIT_NEVER, "tail": FP8_SPLIT_TAIL}
 
 
+def fp8_gemm_noalloc(a: torch.Tensor, fa, sa: torch.Tensor, b: torch.Tensor, fb, sb: torch.Tensor,
+                     out: torch.Tensor, a_layout: str = "rows", b_layout: str = "rows",
+                     split: str = "auto") -> torch.Tensor:
+    """fp8_gemm with a workspace, the split's partials in the library's own
+    device scratch (fp8_gemm_noalloc): no device memory is allocated, so
+    `out` is required. Calls that overlap on one GPU share that scratch."""
+    if out is None:
+        raise ValueError("fp8_gemm_noalloc needs the output tensor")
+    g, out = _gemm_args(a, fa, sa, b, fb, sb, out, a_layout, b_layout)
+    check(load().fp8_gemm_noalloc(g.A, g.fa, g.la, g.sa, g.B, g.fb, g.lb, g.sb, g.M, g.N, g.R, g.C, SPLITS[split],
+                                  _stream(a)), "fp8_gemm_noalloc")
+    return out
+
+
 def gemm_workspace_bytes(fa, fb, M: int, N: int, R: int, split: str = "auto") -> int:
     """Workspace bytes fp8_gemm(..., workspace=, split=) uses for this GEMM
     on the current device (0: it would not split)."""

@@ -180,6 +180,20 @@ fp8_status fp8_gemm_ws(const uint8_t* A, fp8_fmt fa, fp8_layout la, const fp8_sc
                                    C_bf16, (int)split, workspace, workspace_bytes, stream));
 }
 
+fp8_status fp8_gemm_noalloc(const uint8_t* A, fp8_fmt fa, fp8_layout la, const fp8_scale_t* sa, const uint8_t* B,
+                            fp8_fmt fb, fp8_layout lb, const fp8_scale_t* sb, int64_t M, int64_t N, int64_t R,
+                            void* C_bf16, fp8_split split, hipStream_t stream) {
+  const fp8_status st = check_gemm(A, fa, la, sa, B, fb, lb, sb, M, N, R, C_bf16);
+  if (st != FP8_OK) return st;
+  if (split != FP8_SPLIT_AUTO && split != FP8_SPLIT_NEVER && split != FP8_SPLIT_TAIL) return FP8_ERR_INVALID;
+  void* ws = nullptr;
+  size_t cap = 0;
+  if (static_scratch(&ws, &cap) != hipSuccess) return FP8_ERR_HIP;
+  if (gemm_tail_split(fa, fb, M, N, R, (int)split).bytes > cap) return FP8_ERR_UNSUPPORTED;
+  return hip_status(launch_gemm_ws(A, fa, la == FP8_OPERAND_COLS, sa, B, fb, lb == FP8_OPERAND_COLS, sb, M, N, R,
+                                   C_bf16, (int)split, ws, cap, stream));
+}
+
 fp8_status fp8_gemm_pair(const fp8_gemm_args* first, const fp8_gemm_args* second, hipStream_t stream) {
   if (!first || !second) return FP8_ERR_INVALID;
   GemmDesc g[2];

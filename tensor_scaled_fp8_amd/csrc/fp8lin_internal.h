@@ -156,6 +156,13 @@ TailSplit gemm_tail_split(int fa, int fb, int64_t M, int64_t N, int64_t R, int m
 hipError_t launch_gemm_ws(const uint8_t* A, int fa, bool ta, const fp8_scale_t* sa, const uint8_t* B, int fb,
                           bool tb, const fp8_scale_t* sb, int64_t M, int64_t N, int64_t R, void* C, int mode,
                           void* ws, size_t ws_bytes, hipStream_t st);
+// The device's static scratch of fp8_gemm_noalloc (its address on the
+// current device, looked up once per device, and its size in bytes): room
+// for the tail split of kStaticTailTiles tiles, the most a last wave at
+// most half full holds on a 256-CU device.
+constexpr int kStaticTailTiles = 128;
+constexpr int kMaxDevices = 64;
+hipError_t static_scratch(void** ptr, size_t* bytes);
 // One GEMM of a pair (the arguments of launch_gemm).
 struct GemmDesc {
   const uint8_t* A;

@@ -59,6 +59,7 @@
 //    last wave at most half full into two reduction halves
 //    (gemm_tailsplit_kernel: FP32 partials in a caller workspace, added by
 //    gemm_tail_fixup_kernel), with the per-tile arithmetic unchanged.
+#include <mutex>
 #include <type_traits>
 
 #include "fp8lin_internal.h"
@@ -838,6 +839,35 @@ hipError_t launch_gemm_ws(const uint8_t* A, int fa, bool ta, const fp8_scale_t* 
   if (!ta && tb) return launch_tailsplit<false, true>(A, sa, B, sb, M, N, R, C, ts, part, st);
   if (ta && !tb) return launch_tailsplit<true, false>(A, sa, B, sb, M, N, R, C, ts, part, st);
   return launch_tailsplit<true, true>(A, sa, B, sb, M, N, R, C, ts, part, st);
+}
+
+// Scratch memory of fp8_gemm_noalloc: the tail split's FP32 partials for
+// up to kStaticTailTiles tiles (two 256 x 256 halves each), held in the
+// code object's own device memory, so a call needs no workspace from the
+// caller and allocates nothing. Each device that loads the library holds
+// its own copy until the process ends. Host code never uses the array's
+// name as an address: static_scratch() asks the runtime for this device's
+// address once and keeps it.
+constexpr size_t kStaticScratchBytes = (size_t)kStaticTailTiles * 2 * 65536 * sizeof(float);
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+hipError_t static_scratch(void** ptr, size_t* bytes) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {nullptr};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  *bytes = kStaticScratchBytes;
+  return hipSuccess;
 }
 
 hipError_t launch_gemm_wgrad_amax(const uint8_t* A, bool ta, const fp8_scale_t* sa, const uint8_t* B, bool tb,

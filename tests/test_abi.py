@@ -31,7 +31,7 @@ def test_header_functions_all_exported():
     for n in names:
         assert hasattr(lib, n), n
         assert n in _lib.SIGNATURES, f"binding lacks {n}"
-    assert lib.fp8_abi_version() == 10
+    assert lib.fp8_abi_version() == 11
 
 
 def test_status_strings():
@@ -123,6 +123,14 @@ def test_argument_validation_without_launch():
               None) == INV
     assert gw(_vp(ok), 0, 0, None, _vp(ok), 0, 1, _vp(ok), 16, 16, 16, _vp(ok), 0, None, 0, None) == INV
     assert gw(_vp(ok), 0, 0, _vp(ok), _vp(ok), 0, 1, _vp(ok), 16, 16, 16, _vp(ok), 3, None, 0, None) == INV
+    # no-allocation GEMM: fp8_gemm's checks and the split enum, before any device access
+    gn = lib.fp8_gemm_noalloc
+    assert gn(_vp(ok), 0, 0, _vp(ok), _vp(ok), 0, 1, _vp(ok), 16, 16, 24, _vp(ok), 0, None) == UNS
+    assert gn(_vp(ok), 0, 0, None, _vp(ok), 0, 1, _vp(ok), 16, 16, 16, _vp(ok), 0, None) == INV
+    assert gn(_vp(ok), 0, 0, _vp(ok), _vp(ok), 0, 1, _vp(ok), 16, 16, 16, _vp(ok), 3, None) == INV
+    assert gn(_vp(ok), 0, 2, _vp(ok), _vp(ok), 0, 1, _vp(ok), 16, 16, 16, _vp(ok), 0, None) == INV
+    assert gn(_vp(ok), 0, 0, _vp(ok), _vp(ok), 0, 1, _vp(ok), 16, 16, 16, _vp(ok + 2), 0, None) == INV
+    assert _lib.FP8_NOALLOC_SCRATCH_BYTES == 128 * 2 * 65536 * 4
     wb = lib.fp8_gemm_workspace_bytes
     TAIL, AUTO, NEVER = _lib.FP8_SPLIT_TAIL, _lib.FP8_SPLIT_AUTO, _lib.FP8_SPLIT_NEVER
     assert wb(0, 0, 256, 256, 1024, TAIL) == 2 * 65536 * 4      # one tile: its two halves' FP32 partials
