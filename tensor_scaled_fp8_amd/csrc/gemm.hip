@@ -80,7 +80,6 @@ constexpr int kBK = 128;                         // k-bytes per stage (one cache
 constexpr int kThreads = 256;
 constexpr int kGroupM = 8;                       // tile rows per raster group
 constexpr int kOpBytes = kBM * kBK;              // 32 KB: the A (or B) part of a stage
-constexpr int kStageBytes = 2 * kOpBytes;        // 64 KB; two stage buffers
 constexpr int kRsrcWord3 = 0x00020000;           // buffer resource word 3 for raw byte loads (gfx9 family)
 
 #define LDS_AS __attribute__((address_space(3)))
@@ -142,13 +141,39 @@ struct GemmParams {
   int M, N, R, tiles_m, tiles_n;
 };
 
-// The two stage buffers (also the epilogue's staging of C). They are
-// separate LDS objects, always addressed with a compile-time index, so the
-// compiler can tell the buffer being read from the one with loads in flight
-// and does not wait for those. Declared once for the file, so a kernel that
-// runs tiles of two GEMM variants still holds 128 KB.
-__shared__ uint4 g_slot0[kStageBytes / 16];
-__shared__ uint4 g_slot1[kStageBytes / 16];
+// Stage buffers: two slots for A's part of a stage and three for B's
+// (32 KB each, 160 KB in all, the whole LDS of a CU), so B's loads are
+// issued a stage earlier than A's. B is the operand streamed from HBM on
+// the layer shapes (the weights in the forward and dgrad GEMMs, the
+// gradient in the wgrad), whose latency one stage of lead did not cover.
+// They are separate LDS objects, always addressed with a compile-time
+// index, so the compiler can tell a slot being read from one with loads in
+// flight and does not wait for those. Four of them (A0, A1, B0, B1) also
+// stage the epilogue's C tile, the fifth holds its wave maxima. Declared
+// once for the file, so a kernel that runs tiles of two GEMM variants still
+// holds 160 KB.
+__shared__ uint4 g_a0[kOpBytes / 16];
+__shared__ uint4 g_a1[kOpBytes / 16];
+__shared__ uint4 g_b0[kOpBytes / 16];
+__shared__ uint4 g_b1[kOpBytes / 16];
+__shared__ uint4 g_b2[kOpBytes / 16];
+
+// A slot of stage s (s % 2) and B slot (s % 3), for compile-time s
+template <int S>
+__device__ inline lds_u8* a_slot() {
+  if constexpr (S % 2 == 0) return (lds_u8*)g_a0;
+  else return (lds_u8*)g_a1;
+}
+template <int S>
+__device__ inline lds_u8* b_slot() {
+  if constexpr (S % 3 == 0) return (lds_u8*)g_b0;
+  else if constexpr (S % 3 == 1) return (lds_u8*)g_b1;
+  else return (lds_u8*)g_b2;
+}
+// 32 KB region j (0..3) of the epilogue's C staging: A0, A1, B0, B1
+__device__ inline lds_u8* c_region(int j) {
+  return j == 0 ? (lds_u8*)g_a0 : j == 1 ? (lds_u8*)g_a1 : j == 2 ? (lds_u8*)g_b0 : (lds_u8*)g_b1;
+}
 
 // AMAX: the epilogue also takes max |C| over the bf16 values it writes and
 // merges (tag << 16) | max into s_out->gen_max (one atomic per block, as the
@@ -190,12 +215,6 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, fp8_sca
   const fp8_scale_t* __restrict__ sb = p.sb;
   uint16_t* __restrict__ C = p.C;
   const int M = p.M, N = p.N, R = p.R, tiles_m = p.tiles_m, tiles_n = p.tiles_n;
-  auto slot = [&](auto J_) -> lds_u8* {
-    if constexpr ((decltype(J_)::value & 1) == 0) return (lds_u8*)g_slot0;
-    else return (lds_u8*)g_slot1;
-  };
-  using S0 = std::integral_constant<int, 0>;
-  using S1 = std::integral_constant<int, 1>;
 
   // ---- tile selection: XCD-contiguous ranges, grouped raster inside ----
   int m0, n0;
@@ -255,53 +274,68 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, fp8_sca
       __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, (int)((uint32_t)M * (uint32_t)R), kRsrcWord3);
   const __amdgpu_buffer_rsrc_t rsb =
       __builtin_amdgcn_make_buffer_rsrc((void*)B, (short)0, (int)((uint32_t)N * (uint32_t)R), kRsrcWord3);
-  // the 16 loads (8 of A, 8 of B) of one full stage
-  auto issue_full = [&](lds_u8* sl, int stage) {
+  // the 8 loads of A's (or B's) part of one full stage into slot sl. A
+  // stage past the last full one (stage >= nfull) is loaded through a
+  // resource of zero bytes: every lane is out of range, so nothing is read
+  // from memory and zeros land in the slot, which no later read uses; the
+  // loads still count in vmcnt, so the steady-state wait stays exact up to
+  // the last stage.
+  auto issue_a = [&](lds_u8* sl, int stage) {
     // wave-uniform; below 2^32 (operands are below 4 GiB), passed as int
     const int koffa = (int)((uint32_t)(s0 + stage) * kBK * (TA ? (uint32_t)M : 1u));
-    const int koffb = (int)((uint32_t)(s0 + stage) * kBK * (TB ? (uint32_t)N : 1u));
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)A, (short)0, stage < nfull ? (int)((uint32_t)M * (uint32_t)R) : 0, kRsrcWord3);
     lds_u8* sa_ = sl + (8 * w) * 1024;
-    lds_u8* sb_ = sl + kOpBytes + (8 * w) * 1024;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (LDS_AS void*)(sa_ + i * 1024), 16, (int)offa[i], koffa, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (LDS_AS void*)(sb_ + i * 1024), 16, (int)offb[i], koffb, 0, 0);
-    }
+    for (int i = 0; i < 8; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(sa_ + i * 1024), 16, (int)offa[i], koffa, 0, 0);
   };
-  // any stage, including a partial last one (k past R zero-filled)
-  auto issue_any = [&](lds_u8* sl, int stage) {
+  auto issue_b = [&](lds_u8* sl, int stage) {
+    const int koffb = (int)((uint32_t)(s0 + stage) * kBK * (TB ? (uint32_t)N : 1u));
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)B, (short)0, stage < nfull ? (int)((uint32_t)N * (uint32_t)R) : 0, kRsrcWord3);
+    lds_u8* sb_ = sl + (8 * w) * 1024;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(sb_ + i * 1024), 16, (int)offb[i], koffb, 0, 0);
+  };
+  // any stage, including a partial last one (k past R zero-filled): A's
+  // part (B = false) or B's part (B = true) into slot sl
+  auto issue_any = [&](auto B_, lds_u8* sl, int stage) {
+    constexpr bool IsB = decltype(B_)::value;
     if (stage < nfull) {
-      issue_full(sl, stage);
+      if constexpr (IsB) issue_b(sl, stage);
+      else issue_a(sl, stage);
       return;
     }
+    constexpr bool T = IsB ? TB : TA;
     const int k0 = (s0 + stage) * kBK;
-    lds_u8* sa_ = sl + (8 * w) * 1024;
-    lds_u8* sb_ = sl + kOpBytes + (8 * w) * 1024;
-    // first k of lane's 16 bytes (row layout) or lane's k-row (reduction-major)
-    auto lane_k = [&](auto T_, int i) -> int {
-      if constexpr (!decltype(T_)::value) {
-        const int row = 8 * (8 * w + i) + (lane >> 3);
-        return k0 + 16 * ((lane & 7) ^ swz(row));
-      } else {
-        return k0 + 4 * (8 * w + i) + (lane >> 4);
-      }
-    };
+    lds_u8* dst = sl + (8 * w) * 1024;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      lds_u8* da = sa_ + i * 1024;
-      lds_u8* db = sb_ + i * 1024;
-      if (lane_k(TAc{}, i) < R)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (LDS_AS void*)da, 16, (int)offa[i],
-                                                 (int)((uint32_t)k0 * (TA ? (uint32_t)M : 1u)), 0, 0);
-      else
-        *(lds_u32x4*)(da + 16 * lane) = (u32x4){0, 0, 0, 0};
-      if (lane_k(TBc{}, i) < R)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (LDS_AS void*)db, 16, (int)offb[i],
-                                                 (int)((uint32_t)k0 * (TB ? (uint32_t)N : 1u)), 0, 0);
-      else
-        *(lds_u32x4*)(db + 16 * lane) = (u32x4){0, 0, 0, 0};
+      lds_u8* d = dst + i * 1024;
+      // first k of lane's 16 bytes (row layout) or lane's k-row (reduction-major)
+      int lk;
+      if constexpr (!T) {
+        const int row = 8 * (8 * w + i) + (lane >> 3);
+        lk = k0 + 16 * ((lane & 7) ^ swz(row));
+      } else {
+        lk = k0 + 4 * (8 * w + i) + (lane >> 4);
+      }
+      if (lk < R) {
+        if constexpr (IsB)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (LDS_AS void*)d, 16, (int)offb[i],
+                                                   (int)((uint32_t)k0 * (TB ? (uint32_t)N : 1u)), 0, 0);
+        else
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (LDS_AS void*)d, 16, (int)offa[i],
+                                                   (int)((uint32_t)k0 * (TA ? (uint32_t)M : 1u)), 0, 0);
+      } else {
+        *(lds_u32x4*)(d + 16 * lane) = (u32x4){0, 0, 0, 0};
+      }
     }
   };
+  using IsA = std::false_type;
+  using IsB = std::true_type;
 
   // ---- fragment reads: lane -> row (lane & 31); step h (0, 1) of a stage
   // takes logical chunks 4h + 2g and 4h + 2g + 1, g = lane >> 5. swz() of
@@ -334,9 +368,9 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, fp8_sca
     for (int f4 = 0; f4 < 4; ++f4)
       toff[f4] = (32 * (G >> 1) + r) * 256 + (((2 * f4 + (G & 1)) ^ r) << 4) + 8 * (j & 1);
   }
-  // wave-uniform fragment bases of A and B
+  // wave-uniform fragment bases of A and B within their slots
   const int a_row0 = TA ? 128 * wm : 128 * wm * kBK;
-  const int b_row0 = kOpBytes + (TB ? 128 * wn : 128 * wn * kBK);
+  const int b_row0 = TB ? 128 * wn : 128 * wn * kBK;
   struct Frags {
     v8i a[4], b[4];
   };
@@ -358,16 +392,16 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, fp8_sca
     }
     return v;
   };
-  auto read_step = [&](const lds_u8* sl, int h, Frags& f) {
+  auto read_step = [&](const lds_u8* sla, const lds_u8* slb, int h, Frags& f) {
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
-      if constexpr (TA) f.a[mi] = read_frag_t(sl + a_row0, h, mi);
-      else f.a[mi] = read_frag(sl + a_row0 + 32 * mi * kBK, h);
+      if constexpr (TA) f.a[mi] = read_frag_t(sla + a_row0, h, mi);
+      else f.a[mi] = read_frag(sla + a_row0 + 32 * mi * kBK, h);
     }
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni) {
-      if constexpr (TB) f.b[ni] = read_frag_t(sl + b_row0, h, ni);
-      else f.b[ni] = read_frag(sl + b_row0 + 32 * ni * kBK, h);
+      if constexpr (TB) f.b[ni] = read_frag_t(slb + b_row0, h, ni);
+      else f.b[ni] = read_frag(slb + b_row0 + 32 * ni * kBK, h);
     }
   };
   // LDS reads per step, spread evenly over its first 8 MFMAs below
@@ -399,32 +433,42 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, fp8_sca
                                                                        0, 0, 0, 0);
   };
 
-  // Software pipeline. Stage s lives in buffer s % 2; its two MFMA steps use
-  // fr[0] (k-half 0) and fr[1] (k-half 1). On entry to stage s, fr[0] holds
-  // its first half and stage s+1's loads are in flight.
+  // Software pipeline. Stage s lives in A slot s % 2 and B slot s % 3; its
+  // two MFMA steps use fr[0] (k-half 0) and fr[1] (k-half 1). On entry to
+  // stage s, fr[0] holds its first half, and the loads in flight are A of
+  // stage s+1, then B of stage s+2 (B of stage s+1 was issued a stage
+  // before them).
   //  step 2s:   read k-half 1 of stage s into fr[1]; MFMAs on fr[0].
-  //  step 2s+1: wait for stage s+1 (own loads by vmcnt, everyone's by the
-  //             barrier, which also follows every wave's reads of buffer
-  //             s % 2); issue stage s+2 into buffer s % 2; read k-half 0 of
-  //             stage s+1 into fr[0]; MFMAs on fr[1].
+  //  step 2s+1: wait for stage s+1 (own loads by vmcnt: all but the last
+  //             8, which are B of stage s+2; everyone's by the barrier,
+  //             which also follows every wave's reads of stage s); issue A
+  //             of stage s+2 and B of stage s+3 into the slots stage s
+  //             freed; read k-half 0 of stage s+1 into fr[0]; MFMAs on fr[1].
   Frags fr[2];
-  if (nk > 0) issue_any(slot(S0{}), 0);
-  if (nk > 1) issue_any(slot(S1{}), 1);
-  if (nk > 0) {
-    if (nk > 1) {
-      if (nfull > 1) wait_vmcnt<16>();  // full stage 1 (16 loads) may stay in flight
-      else wait_vmcnt<0>();                      // partial stage 1: count not exact
-    } else {
-      wait_vmcnt<0>();
+  {
+    if (nk > 0) {
+      issue_any(IsA{}, a_slot<0>(), 0);
+      issue_any(IsB{}, b_slot<0>(), 0);
     }
-    block_sync_lds();
-    read_step(slot(S0{}), 0, fr[0]);
+    if (nk > 1) {
+      issue_any(IsA{}, a_slot<1>(), 1);
+      issue_any(IsB{}, b_slot<1>(), 1);
+    }
+    if (nk > 2) issue_any(IsB{}, b_slot<2>(), 2);
+    if (nk > 0) {
+      if (nfull >= 3) wait_vmcnt<24>();  // stages 1 and 2 full: their 24 loads may stay in flight
+      else wait_vmcnt<0>();              // a partial stage among them: count not exact
+      block_sync_lds();
+      read_step(a_slot<0>(), b_slot<0>(), 0, fr[0]);
+    }
   }
-  // steady state: stages s+1 and s+2 are full. Hard scheduling fences keep
-  // the order; the group hints interleave reads / loads with the MFMAs.
+  // One stage in the steady state, with compile-time slots (J: the stage
+  // index mod 6): the loads of A of stage s+2 and B of s+3 are issued (from
+  // nothing when past the last stage, see issue_a). Hard scheduling fences
+  // keep the order; the group hints interleave reads / loads with the MFMAs.
   auto stage_main = [&](auto J_, int s) {
     constexpr int J = decltype(J_)::value;
-    read_step(slot(J_), 1, fr[1]);
+    read_step(a_slot<J>(), b_slot<J>(), 1, fr[1]);
     mfma_all(fr[0]);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -434,11 +478,12 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, fp8_sca
 #pragma unroll
     for (int i = 0; i < 8; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     __builtin_amdgcn_sched_barrier(0);
-    wait_vmcnt<0>();   // stage s+1 landed (the only loads in flight)
-    block_sync_lds();  // everyone's loads landed, everyone's reads of buffer J done
+    wait_vmcnt<8>();   // A of stage s+1 landed (and B of s+1, issued before it); B of s+2 may fly
+    block_sync_lds();  // everyone's loads landed, everyone's reads of stage s's slots done
     __builtin_amdgcn_sched_barrier(0);
-    issue_full(slot(J_), s + 2);
-    read_step(slot(std::integral_constant<int, J + 1>{}), 0, fr[0]);
+    issue_a(a_slot<J>(), s + 2);
+    issue_b(b_slot<J>(), s + 3);
+    read_step(a_slot<J + 1>(), b_slot<J + 1>(), 0, fr[0]);
     mfma_all(fr[1]);
     // one load per MFMA: in bursts of two per MFMA the four waves' loads
     // outran the load path and stalled issue (measured 2-3 % slower)
@@ -455,29 +500,53 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, fp8_sca
     }
     __builtin_amdgcn_sched_barrier(0);
   };
-  // general stage (tail, at most a few stages): bounds on every stage, all
-  // loads awaited in full, so the buffers are picked at run time; zero-filled
-  // parts of a partial stage are LDS stores, made visible by the next
-  // barrier (block_sync_lds waits for this wave's LDS accesses first)
+  // general stage (the last three when one of them is partial, or all of
+  // them when there are fewer than three full stages):
+  // bounds on every stage, all loads awaited in full, so the slots are
+  // picked at run time; zero-filled parts of a partial stage are LDS
+  // stores, made visible by the next barrier (block_sync_lds waits for
+  // this wave's LDS accesses first)
   auto stage_any = [&](int s) {
-    lds_u8* cur = (s & 1) ? slot(S1{}) : slot(S0{});
-    lds_u8* nxt = (s & 1) ? slot(S0{}) : slot(S1{});
-    read_step(cur, 1, fr[1]);
+    lds_u8* const as[2] = {a_slot<0>(), a_slot<1>()};
+    lds_u8* const bs[3] = {b_slot<0>(), b_slot<1>(), b_slot<2>()};
+    read_step(as[s & 1], bs[s % 3], 1, fr[1]);
     mfma_all(fr[0]);
     if (s + 1 < nk) {
       wait_vmcnt<0>();
       block_sync_lds();
-      if (s + 2 < nk) issue_any(cur, s + 2);
-      read_step(nxt, 0, fr[0]);
+      if (s + 2 < nk) issue_any(IsA{}, as[s & 1], s + 2);
+      if (s + 3 < nk) issue_any(IsB{}, bs[s % 3], s + 3);
+      read_step(as[(s + 1) & 1], bs[(s + 1) % 3], 0, fr[0]);
     }
     mfma_all(fr[1]);
   };
-  const int main_stages = nfull > 2 ? (nfull - 2) & ~1 : 0;  // even: buffer index is compile-time
+  // Stages in the steady state: all of them when every stage is full (the
+  // last ones load nothing, see issue_a), else those before the last three
+  // full ones; whole rounds of six (slot indices repeat every six stages),
+  // then the rest one by one. The stages after them take the general path.
+  const int main_stages = (nk == nfull && nfull >= 3) ? nfull : (nfull > 3 ? nfull - 3 : 0);
   int s = 0;
-  for (; s < main_stages; s += 2) {
-    stage_main(S0{}, s);
-    stage_main(S1{}, s + 1);
+  using J0 = std::integral_constant<int, 0>;
+  using J1 = std::integral_constant<int, 1>;
+  using J2 = std::integral_constant<int, 2>;
+  using J3 = std::integral_constant<int, 3>;
+  using J4 = std::integral_constant<int, 4>;
+  using J5 = std::integral_constant<int, 5>;
+  for (; s + 6 <= main_stages; s += 6) {
+    stage_main(J0{}, s);
+    stage_main(J1{}, s + 1);
+    stage_main(J2{}, s + 2);
+    stage_main(J3{}, s + 3);
+    stage_main(J4{}, s + 4);
+    stage_main(J5{}, s + 5);
   }
+  const int rest = main_stages - s;
+  if (rest > 0) stage_main(J0{}, s);
+  if (rest > 1) stage_main(J1{}, s + 1);
+  if (rest > 2) stage_main(J2{}, s + 2);
+  if (rest > 3) stage_main(J3{}, s + 3);
+  if (rest > 4) stage_main(J4{}, s + 4);
+  s = main_stages;
   for (; s < nk; ++s) stage_any(s);
   wait_vmcnt<0>();
   block_sync_lds();
@@ -518,7 +587,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, fp8_sca
 #pragma unroll
     for (int mi = MLO; mi < MLO + 2; ++mi) {
       const int row = 128 * wm + 32 * mi + frow;
-      lds_u8* crow = (wm ? slot(S1{}) : slot(S0{})) + (mi >> 1) * (kStageBytes / 2) + (row & 63) * 512;
+      lds_u8* crow = c_region(2 * wm + (mi >> 1)) + (row & 63) * 512;
 #pragma unroll
       for (int ni = 0; ni < 4; ++ni) {
 #pragma unroll
@@ -595,14 +664,14 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, fp8_sca
     }
     return r;
   };
-  __shared__ uint32_t wmax[2][kThreads / 64];
+  uint32_t(*wmax)[kThreads / 64] = (uint32_t(*)[kThreads / 64])g_b2;  // the slot C staging leaves free
   if constexpr (AMAX) {
     const uint32_t r = wave_max();
     if (lane == 0) wmax[0][w] = r;
     cmax = (u16x2){0, 0};
   }
   block_sync_lds();
-  drain_pair(slot(S0{}), 0, slot(S1{}), 2);
+  drain_pair(c_region(0), 0, c_region(2), 2);
   stage(M2{});
   if constexpr (AMAX) {
     const uint32_t r = wave_max();
@@ -621,7 +690,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, fp8_sca
       if (tile == 0) s_out->sat_count = 0u;
     }
   }
-  drain_pair(slot(S0{}) + kStageBytes / 2, 1, slot(S1{}) + kStageBytes / 2, 3);
+  drain_pair(c_region(1), 1, c_region(3), 3);
 }
 
 // One GEMM: one block per output tile.
@@ -675,12 +744,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tail_fixup_kernel(GemmParams
   const int shift = -(p.sa->bias + p.sb->bias);
   const float* h0 = part + (size_t)(2 * j) * 65536 + 4 * t;
   const float* h1 = h0 + 65536;
-  lds_u8* const lds0 = (lds_u8*)g_slot0;
-  lds_u8* const lds1 = (lds_u8*)g_slot1;
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi) {
     const int row = 128 * wm + 32 * mi + frow;
-    lds_u8* crow = (wm ? lds1 : lds0) + (mi >> 1) * (kStageBytes / 2) + (row & 63) * 512;
+    lds_u8* crow = c_region(2 * wm + (mi >> 1)) + (row & 63) * 512;
     f32x4 a[16], b[16];
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
@@ -708,7 +775,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tail_fixup_kernel(GemmParams
   const bool col_ok = n0 + 8 * c < N;
 #pragma unroll
   for (int reg = 0; reg < 4; ++reg) {
-    const lds_u8* src = (reg >> 1 ? lds1 : lds0) + (reg & 1) * (kStageBytes / 2);
+    const lds_u8* src = c_region(2 * (reg >> 1) + (reg & 1));
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const int r = r0 + 8 * k;  // row within the 64-row region
