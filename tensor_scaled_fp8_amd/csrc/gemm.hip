@@ -455,6 +455,13 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, fp8_sca
       issue_any(IsB{}, b_slot<1>(), 1);
     }
     if (nk > 2) issue_any(IsB{}, b_slot<2>(), 2);
+    // the accumulators are zeroed here, while the first loads are in
+    // flight: left to the compiler, the 256 writes sat between the wait for
+    // stage 0 and the first MFMA (~0.5 us per tile)
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni) asm volatile("" : "+a"(acc[mi][ni]));
     if (nk > 0) {
       if (nfull >= 3) wait_vmcnt<24>();  // stages 1 and 2 full: their 24 loads may stay in flight
       else wait_vmcnt<0>();              // a partial stage among them: count not exact
