@@ -489,7 +489,8 @@ def spec_stream(tsf, torch, lin, margin, mu, step, steps, flops, g, sig):
 def inference_pass(tsf, torch, lin, margin, steps, warmup):
     """Forward-only inference on weights cast once (post-training
     quantisation): per linear, fp8_linear_fwd_cached = X quantised (amax
-    rule, or a fixed FP8-CSCALE bias) + the forward GEMM on the cached w8t.
+    rule, or a fixed FP8-CSCALE bias) + the forward GEMM on the cached
+    row-major w8 (read reduction-major, as in training).
     Reported beside the training step, not part of its value."""
     out = {}
     flops = sum(2 * d["L"].M * d["L"].K * d["L"].N for d in lin)
@@ -503,8 +504,8 @@ def inference_pass(tsf, torch, lin, margin, steps, warmup):
 
         def fwd():
             for i, d in enumerate(lin):
-                w8t, sw = prepared[i]
-                tsf.fp8_linear_fwd_cached(d["X"], w8t, sw, d["ws"].x8, recs[i], margin, mode, Y=d["Y"])
+                w8, sw = prepared[i]
+                tsf.fp8_linear_fwd_cached(d["X"], w8, sw, d["ws"].x8, recs[i], margin, mode, Y=d["Y"])
         for _ in range(warmup):
             fwd()
         torch.cuda.synchronize()

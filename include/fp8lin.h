@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define FP8LIN_ABI_VERSION 11
+#define FP8LIN_ABI_VERSION 12
 
 typedef enum fp8_fmt {
   FP8_E4M3 = 0, /* OCP E4M3FN: weights and activations [AMAX bullet 4] */
@@ -515,20 +515,23 @@ typedef enum fp8_scaling {
 /*
  * FP8 inference forward with a weight cast once, as in post-training
  * quantisation [AMAX "Proposed method" bullet 5]: Y = X W from a prepared
- * w8t [N,K] (E4M3, e.g. fp8_amax_scale + fp8_cast of W's transposed copy,
- * or fp8_scale_fixed + fp8_cast) and its record sw. Per call only X is
+ * FP8 weight w8 (E4M3, e.g. fp8_amax_scale + fp8_cast, or fp8_scale_fixed
+ * + fp8_cast) and its record sw. lw = FP8_OPERAND_COLS: w8 is the row-major
+ * copy of W [K,N] (the layout the training forward reads, and the faster
+ * one: read reduction-major); FP8_OPERAND_ROWS: w8 is W's transposed copy
+ * [N,K]; another value -> FP8_ERR_INVALID. Per call only X is
  * quantised: with FP8_SCALING_AMAX, amax + bias (margin) + the row-wise cast
  * into x8 with its record written to sx (as fp8_quantize with no transposed
  * output); with FP8_SCALING_FIXED, the row-wise cast with the bias sx holds.
- * Then the forward GEMM. Bit-identical to fp8_linear_fwd's Y when w8t and
- * sw are what fp8_linear_fwd would produce from W.
- *   X [M,K] bf16, Y [M,N] bf16, w8t [N,K] u8, x8 [M,K] u8; device, 16-B
- *   aligned. M, K, N multiples of 16, x8 and w8t below 4 GiB.
+ * Then the forward GEMM. Bit-identical to fp8_linear_fwd's Y (in either
+ * layout) when w8 and sw are what fp8_linear_fwd would produce from W.
+ *   X [M,K] bf16, Y [M,N] bf16, w8 u8, x8 [M,K] u8; device, 16-B
+ *   aligned. M, K, N multiples of 16, x8 and w8 below 4 GiB.
  *   sw: read only. sx: written (AMAX) or read (FIXED); sx == sw ->
  *   FP8_ERR_INVALID. NaNs in X become NaN codes in either mode.
  */
 fp8_status fp8_linear_fwd_cached(const void* X, int64_t M, int64_t K, int64_t N, int margin,
-                                 fp8_scaling x_scaling, const uint8_t* w8t, const fp8_scale_t* sw,
+                                 fp8_scaling x_scaling, const uint8_t* w8, fp8_layout lw, const fp8_scale_t* sw,
                                  uint8_t* x8, fp8_scale_t* sx, void* Y, hipStream_t stream);
 
 #ifdef __cplusplus

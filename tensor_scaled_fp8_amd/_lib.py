@@ -38,8 +38,8 @@ SIGNATURES = {
     "fp8_linear_scratch_bytes": (ctypes.c_size_t, [c_i64, c_i64, c_i64]),
     "fp8_linear_fwd": (c_int, [c_vp, c_vp, c_i64, c_i64, c_i64, c_int, c_vp, c_vp, c_vp]),
     "fp8_linear_bwd": (c_int, [c_vp, c_i64, c_i64, c_i64, c_int, c_int, c_vp, c_vp, c_vp, c_vp]),
-    "fp8_linear_fwd_cached": (c_int, [c_vp, c_i64, c_i64, c_i64, c_int, c_int, c_vp, c_vp, c_vp, c_vp, c_vp,
-                                      c_vp]),
+    "fp8_linear_fwd_cached": (c_int, [c_vp, c_i64, c_i64, c_i64, c_int, c_int, c_vp, c_int, c_vp, c_vp, c_vp,
+                                      c_vp, c_vp]),
     "fp8_wgrad_fp8": (c_int, [c_vp, c_int, c_vp, c_vp, c_int, c_vp, c_i64, c_i64, c_i64, c_int, c_int, c_vp, c_vp,
                               c_vp, c_vp, c_vp]),
     "fp8_adam_init_master": (c_int, [c_i64, c_vp, c_vp, c_vp, c_vp]),
@@ -53,7 +53,7 @@ FP8_OK, FP8_ERR_INVALID, FP8_ERR_UNSUPPORTED, FP8_ERR_HIP = 0, 1, 2, 3
 FLAG_NONFINITE, FLAG_ZERO, FLAG_CLAMPED = 1, 2, 4
 FP8_SCALING_AMAX, FP8_SCALING_FIXED = 0, 1
 FP8_SPLIT_AUTO, FP8_SPLIT_NEVER, FP8_SPLIT_TAIL = 0, 1, 2
-ABI_VERSION = 11
+ABI_VERSION = 12
 FP8_NOALLOC_SCRATCH_BYTES = 128 * 2 * 65536 * 4   # the device scratch of fp8_gemm_noalloc
 
 

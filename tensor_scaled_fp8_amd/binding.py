@@ -447,31 +447,40 @@ def fp8_wgrad_fp8(x8: torch.Tensor, sx: torch.Tensor, dy8: torch.Tensor, sdy: to
     return dW, dw8, dw8t, s_dw
 
 
-def prepare_weight(W: torch.Tensor, margin: int = 0, fixed_bias: Optional[int] = None):
+def prepare_weight(W: torch.Tensor, margin: int = 0, fixed_bias: Optional[int] = None, layout: str = "cols"):
     """Cast a bf16 weight W [K, N] once for inference (post-training
-    quantisation): returns (w8t [N, K] E4M3 codes, record sw). The bias comes
-    from amax(W) and the margin, or is fixed_bias (FP8-CSCALE)."""
+    quantisation): returns (w8, record sw) with w8 the E4M3 codes, row-major
+    [K, N] for layout "cols" (read reduction-major by the forward GEMM, as in
+    training; the faster layout) or transposed [N, K] for "rows". The bias
+    comes from amax(W) and the margin, or is fixed_bias (FP8-CSCALE)."""
     if W.dim() != 2:
         raise ValueError("W must be 2-D")
+    if layout not in LAYOUTS:
+        raise ValueError("layout is 'rows' or 'cols'")
     sw = new_scale(1, W.device)[0]
     if fixed_bias is None:
         fp8_amax_scale(W, "e4m3", sw, margin)
     else:
         fp8_scale_fixed(sw, fixed_bias)
-    _, w8t = fp8_cast(W, "e4m3", sw, rowwise=False, transposed=True)
-    return w8t, sw
+    w8, w8t = fp8_cast(W, "e4m3", sw, rowwise=layout == "cols", transposed=layout == "rows")
+    return (w8 if layout == "cols" else w8t), sw
 
 
-def fp8_linear_fwd_cached(X: torch.Tensor, w8t: torch.Tensor, sw: torch.Tensor, x8: torch.Tensor,
+def fp8_linear_fwd_cached(X: torch.Tensor, w8: torch.Tensor, sw: torch.Tensor, x8: torch.Tensor,
                           sx: torch.Tensor, margin: int = 0, x_scaling: str = "amax",
-                          Y: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Y [M, N] = X [M, K] W from a prepared w8t [N, K] and its record sw.
+                          Y: Optional[torch.Tensor] = None, w_layout: str = "cols") -> torch.Tensor:
+    """Y [M, N] = X [M, K] W from a prepared FP8 weight and its record sw:
+    w8 [K, N] (w_layout "cols", prepare_weight's default) or [N, K] ("rows").
     x_scaling "amax": X's bias from amax(X) and the margin (written to sx);
     "fixed": the bias already in sx (fp8_scale_fixed)."""
-    if X.dim() != 2 or w8t.dim() != 2 or X.shape[1] != w8t.shape[1]:
-        raise ValueError(f"shape mismatch: X {tuple(X.shape)}, w8t {tuple(w8t.shape)}")
+    if w_layout not in LAYOUTS:
+        raise ValueError("w_layout is 'rows' or 'cols'")
+    if X.dim() != 2 or w8.dim() != 2:
+        raise ValueError("X and w8 must be 2-D")
     M, K = X.shape
-    N = w8t.shape[0]
+    Kw, N = (w8.shape[0], w8.shape[1]) if w_layout == "cols" else (w8.shape[1], w8.shape[0])
+    if Kw != K:
+        raise ValueError(f"shape mismatch: X {tuple(X.shape)}, w8 {tuple(w8.shape)} ({w_layout})")
     if tuple(x8.shape) != (M, K):
         raise ValueError("x8 must be [M, K]")
     try:
@@ -481,7 +490,7 @@ def fp8_linear_fwd_cached(X: torch.Tensor, w8t: torch.Tensor, sw: torch.Tensor, 
     if Y is None:
         Y = torch.empty((M, N), dtype=torch.bfloat16, device=X.device)
     check(load().fp8_linear_fwd_cached(_dev(X, torch.bfloat16, "X"), M, K, N, margin, mode,
-                                       _dev(w8t, torch.uint8, "w8t"), _dev(sw, torch.int32, "sw"),
+                                       _dev(w8, torch.uint8, "w8"), LAYOUTS[w_layout], _dev(sw, torch.int32, "sw"),
                                        _dev(x8, torch.uint8, "x8"), _dev(sx, torch.int32, "sx"),
                                        _dev(Y, torch.bfloat16, "Y"), _stream(X)), "fp8_linear_fwd_cached")
     return Y
@@ -496,7 +505,7 @@ class InferenceLinear(torch.nn.Module):
                  x_fixed_bias: Optional[int] = None):
         super().__init__()
         self.margin = margin
-        self.w8t, self.sw = prepare_weight(W, margin, w_fixed_bias)
+        self.w8, self.sw = prepare_weight(W, margin, w_fixed_bias)
         self.sx = new_scale(1, W.device)[0]
         self.x_scaling = "amax"
         if x_fixed_bias is not None:
@@ -509,7 +518,7 @@ class InferenceLinear(torch.nn.Module):
         x2 = x.reshape(-1, shape[-1]).contiguous()
         if self._x8 is None or tuple(self._x8.shape) != tuple(x2.shape):
             self._x8 = torch.empty(x2.shape, dtype=torch.uint8, device=x2.device)
-        y = fp8_linear_fwd_cached(x2, self.w8t, self.sw, self._x8, self.sx, self.margin, self.x_scaling)
+        y = fp8_linear_fwd_cached(x2, self.w8, self.sw, self._x8, self.sx, self.margin, self.x_scaling)
         return y.reshape(*shape[:-1], y.shape[-1])
 
 

@@ -284,22 +284,24 @@ fp8_status fp8_linear_bwd(const void* dY, int64_t M, int64_t K, int64_t N, int m
 }
 
 fp8_status fp8_linear_fwd_cached(const void* X, int64_t M, int64_t K, int64_t N, int margin,
-                                 fp8_scaling x_scaling, const uint8_t* w8t, const fp8_scale_t* sw,
+                                 fp8_scaling x_scaling, const uint8_t* w8, fp8_layout lw, const fp8_scale_t* sw,
                                  uint8_t* x8, fp8_scale_t* sx, void* Y, hipStream_t stream) {
   if (M < 0 || K < 0 || N < 0 || !int_ok(margin)) return FP8_ERR_INVALID;
   if (x_scaling != FP8_SCALING_AMAX && x_scaling != FP8_SCALING_FIXED) return FP8_ERR_INVALID;
+  if (lw != FP8_OPERAND_ROWS && lw != FP8_OPERAND_COLS) return FP8_ERR_INVALID;
   if (!sw || !aligned16(sw) || !sx || !aligned16(sx)) return FP8_ERR_INVALID;
   if (sx == sw) return FP8_ERR_INVALID;  // X's quantise would rewrite the weight's record
   if (M % 16 || K % 16 || N % 16 || M >= kMaxDim || K >= kMaxDim || N >= kMaxDim || !gemm_fits(M, N, K))
     return FP8_ERR_UNSUPPORTED;
   if ((M * K > 0 && (!X || !aligned16(X) || !x8 || !aligned16(x8))) ||
-      (N * K > 0 && (!w8t || !aligned16(w8t))) || (M * N > 0 && (!Y || !aligned16(Y))))
+      (N * K > 0 && (!w8 || !aligned16(w8))) || (M * N > 0 && (!Y || !aligned16(Y))))
     return FP8_ERR_INVALID;
   hipError_t e = x_scaling == FP8_SCALING_AMAX
                      ? launch_quantize(X, M, K, FP8_E4M3, margin, 0, sx, x8, nullptr, stream)
                      : launch_cast(X, M, K, FP8_E4M3, sx, x8, nullptr, stream);
   if (e != hipSuccess) return FP8_ERR_HIP;
-  return hip_status(launch_gemm(x8, FP8_E4M3, false, sx, w8t, FP8_E4M3, false, sw, M, N, K, Y, stream));
+  return hip_status(launch_gemm(x8, FP8_E4M3, false, sx, w8, FP8_E4M3, lw == FP8_OPERAND_COLS, sw, M, N, K, Y,
+                                stream));
 }
 
 fp8_status fp8_wgrad_fp8(const uint8_t* x8, fp8_layout lx, const fp8_scale_t* sx, const uint8_t* dy8,

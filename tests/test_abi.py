@@ -31,7 +31,7 @@ def test_header_functions_all_exported():
     for n in names:
         assert hasattr(lib, n), n
         assert n in _lib.SIGNATURES, f"binding lacks {n}"
-    assert lib.fp8_abi_version() == 11
+    assert lib.fp8_abi_version() == 12
 
 
 def test_status_strings():
@@ -200,8 +200,10 @@ def test_argument_validation_without_launch():
     c = lib.fp8_linear_fwd_cached
     args = lambda **kw: [kw.get(k, d) for k, d in (
         ("X", _vp(ok)), ("M", 16), ("K", 16), ("N", 16), ("margin", 0), ("mode", 0), ("w8t", _vp(ok)),
-        ("sw", _vp(ok)), ("x8", _vp(ok)), ("sx", _vp(ok + 64)), ("Y", _vp(ok)), ("st", None))]
+        ("lw", 1), ("sw", _vp(ok)), ("x8", _vp(ok)), ("sx", _vp(ok + 64)), ("Y", _vp(ok)), ("st", None))]
     assert c(*args(mode=2)) == INV
+    assert c(*args(lw=2)) == INV
+    assert c(*args(lw=-1)) == INV
     assert c(*args(K=24)) == UNS
     assert c(*args(sw=None)) == INV
     assert c(*args(sx=_vp(ok + 8))) == INV

@@ -81,21 +81,22 @@ def _check_y(Y, x_bits, bx, wt_bits, bw):
     assert not bad.any(), (int(bad.sum()), float((err / tol).max()))
 
 
+@pytest.mark.parametrize("layout", ["cols", "rows"])
 @pytest.mark.parametrize("M,K,N", [(272, 400, 528), (16, 16, 16), (512, 768, 3072), (784, 2064, 272)])
-def test_cached_forward_equals_linear_fwd_and_oracle(M, K, N):
+def test_cached_forward_equals_linear_fwd_and_oracle(M, K, N, layout):
     g = np.random.Generator(np.random.PCG64(M + K + N))
     xb = oracle.f64_to_bf16_rne(g.standard_normal((M, K)))
     wb = oracle.f64_to_bf16_rne(g.standard_normal((K, N)) * 0.02)
     X, W = to_dev_bf16(xb), to_dev_bf16(wb)
     ws = tsf.LinearWorkspace(M, K, N, transposed=True)
     Y_train = tsf.fp8_linear_fwd(X, W, ws)
-    w8t, sw = tsf.prepare_weight(W)
+    w8, sw = tsf.prepare_weight(W, layout=layout)
     x8 = torch.empty((M, K), dtype=torch.uint8, device="cuda")
     sx = tsf.new_scale(1)[0]
-    Y = tsf.fp8_linear_fwd_cached(X, w8t, sw, x8, sx)
+    Y = tsf.fp8_linear_fwd_cached(X, w8, sw, x8, sx, w_layout=layout)
     torch.cuda.synchronize()
     assert torch.equal(Y.view(torch.int16), Y_train.view(torch.int16))
-    assert torch.equal(w8t, ws.w8t) and torch.equal(x8, ws.x8)
+    assert torch.equal(w8, ws.w8 if layout == "cols" else ws.w8t) and torch.equal(x8, ws.x8)
     bx = oracle.scale_record(xb, E4M3)["bias"]
     bw = oracle.scale_record(wb, E4M3)["bias"]
     assert (tsf.read_scale(sx)["bias"], tsf.read_scale(sw)["bias"]) == (bx, bw)
@@ -110,13 +111,17 @@ def test_cached_forward_fixed_biases(bx, bw):
     xb = oracle.f64_to_bf16_rne(g.standard_normal((M, K)))
     wb = oracle.f64_to_bf16_rne(g.standard_normal((K, N)) * 0.02)
     X, W = to_dev_bf16(xb), to_dev_bf16(wb)
-    w8t, sw = tsf.prepare_weight(W, fixed_bias=bw)
+    w8t, sw = tsf.prepare_weight(W, fixed_bias=bw, layout="rows")
     sx = tsf.new_scale(1)[0]
     tsf.fp8_scale_fixed(sx, bx)
     x8 = torch.empty((M, K), dtype=torch.uint8, device="cuda")
-    Y = tsf.fp8_linear_fwd_cached(X, w8t, sw, x8, sx, x_scaling="fixed")
+    Y = tsf.fp8_linear_fwd_cached(X, w8t, sw, x8, sx, x_scaling="fixed", w_layout="rows")
     assert np.array_equal(u8(x8), oracle.cast(xb, E4M3, bx)[0])
     assert np.array_equal(u8(w8t), oracle.cast(np.ascontiguousarray(wb.T), E4M3, bw)[0])
+    w8, sw2 = tsf.prepare_weight(W, fixed_bias=bw)          # row-major copy, read reduction-major
+    assert np.array_equal(u8(w8), oracle.cast(wb, E4M3, bw)[0])
+    Y2 = tsf.fp8_linear_fwd_cached(X, w8, sw2, x8, sx, x_scaling="fixed")
+    assert torch.equal(Y2.view(torch.int16), Y.view(torch.int16))
     _check_y(Y, xb, bx, np.ascontiguousarray(wb.T), bw)
 
 
@@ -147,10 +152,10 @@ def test_cached_forward_full_size_gpt7b_up():
     Xd, Wd = to_dev_bf16(X), to_dev_bf16(W)
     ws = tsf.LinearWorkspace(L.M, L.K, L.N)
     Y_train = tsf.fp8_linear_fwd(Xd, Wd, ws)
-    w8t, sw = tsf.prepare_weight(Wd)
+    w8, sw = tsf.prepare_weight(Wd)
     x8 = torch.empty((L.M, L.K), dtype=torch.uint8, device="cuda")
     sx = tsf.new_scale(1)[0]
-    Y = tsf.fp8_linear_fwd_cached(Xd, w8t, sw, x8, sx)
+    Y = tsf.fp8_linear_fwd_cached(Xd, w8, sw, x8, sx)
     torch.cuda.synchronize()
     assert torch.equal(Y.view(torch.int16), Y_train.view(torch.int16))
     r = tsf.read_scale(sx)
@@ -194,12 +199,12 @@ def test_cached_forward_nan_in_x(mode):
         xb[r, c] = v
     wb = oracle.f64_to_bf16_rne(g.standard_normal((K, N)) * 0.02)
     X, W = to_dev_bf16(xb), to_dev_bf16(wb)
-    w8t, sw = tsf.prepare_weight(W, fixed_bias=11)
+    w8t, sw = tsf.prepare_weight(W, fixed_bias=11, layout="rows")
     sx = tsf.new_scale(1)[0]
     if mode == "fixed":
         tsf.fp8_scale_fixed(sx, 0)
     x8 = torch.empty((M, K), dtype=torch.uint8, device="cuda")
-    Y = tsf.fp8_linear_fwd_cached(X, w8t, sw, x8, sx, x_scaling=mode)
+    Y = tsf.fp8_linear_fwd_cached(X, w8t, sw, x8, sx, x_scaling=mode, w_layout="rows")
     bx = 0                                      # fixed 0; the amax rule gives 0 with FLAG_NONFINITE
     if mode == "amax":
         r = tsf.read_scale(sx)
