@@ -18,20 +18,20 @@
 //  * 256 x 256 output tile per 256-thread block (4 waves, 2 x 2), each wave
 //    128 x 128 = 4 x 4 MFMA blocks (256 FP32 accumulators per lane, held in
 //    the accumulation registers).
-//  * Operands stream through two 64 KB LDS buffers, each holding one stage
-//    of k = 128 bytes (256 rows of A and of B). 128 bytes is one cache line
-//    per row: a 16-byte-per-lane load then covers 8 whole lines, which the
-//    load path handles markedly faster than 16 half lines. Global memory is
-//    copied straight into LDS by buffer loads with the LDS-write form (no
-//    register staging); a stage is loaded while the previous one is
-//    multiplied.
+//  * Operands stream through LDS in stages of k = 128 bytes (256 rows of A
+//    and of B, 32 KB each), held in two slots for A and three for B (160 KB),
+//    so B, the operand streamed from HBM, is loaded two stages ahead and A
+//    one. 128 bytes is one cache line per row: a 16-byte-per-lane load then
+//    covers 8 whole lines, which the load path handles markedly faster than
+//    16 half lines. Global memory is copied straight into LDS by buffer
+//    loads with the LDS-write form (no register staging).
 //  * Each stage is two MFMA steps of k = 64 (16 MFMAs per wave each). With
 //    one wave per SIMD nothing else hides the non-MFMA work, so the steps
 //    are software-pipelined: fragments of the next step are read from LDS
 //    into a second register set under the current step's MFMAs. One
 //    barrier per stage: at the second step of stage s, stage s+1 is awaited,
-//    and the loads of stage s+2 go into stage s's buffer, whose fragments
-//    every wave has read by then.
+//    and the loads of A of stage s+2 and B of stage s+3 go into the slots of
+//    stage s, whose fragments every wave has read by then.
 //  * A load writes lane l's 16 bytes at slot l of a 1 KB LDS block (8 rows
 //    x 128 bytes), so the bank swizzle is applied on the source side: the
 //    lane for LDS chunk p of row r fetches global chunk p ^ swz(r).
@@ -39,11 +39,11 @@
 //  * The MFMA is fed B as its first operand and A as its second, so it
 //    produces C^T blocks: each lane then holds 4 runs of 4 consecutive
 //    output columns of one row. The epilogue scales by 2^-(ba+bb), packs
-//    pairs to bf16 with the hardware round-to-nearest-even converter,
-//    stages the tile in LDS and writes C in whole rows (scattered 8-byte
-//    stores would leave partial cache lines and multiply HBM writes), in
-//    two halves so that the first half's stores overlap the second half's
-//    conversions.
+//    pairs to bf16 with the hardware round-to-nearest-even converter, and
+//    each wave stages its block in LDS a quarter at a time and writes C in
+//    whole 256-byte row pieces (scattered 8-byte stores would leave partial
+//    cache lines and multiply HBM writes); a quarter's stores drain while
+//    the next is converted.
 //  * Tiles are numbered so that each XCD (workgroups are dealt round-robin
 //    over the 8 XCDs) works on one contiguous, row-grouped region of C and
 //    its operand panels stay in that XCD's L2.
@@ -114,14 +114,6 @@ __device__ inline void static_for(F&& f) {
   }
 }
 
-__device__ inline void block_sync() {
-  // workgroup barrier only (no wait for this wave's LDS accesses); the empty
-  // asm keeps the compiler from moving memory accesses across it
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 __device__ inline void block_sync_lds() {
   // all LDS writes of this wave done, then the workgroup barrier; the empty
   // asm keeps the compiler from moving memory accesses across it
@@ -148,10 +140,10 @@ struct GemmParams {
 // gradient in the wgrad), whose latency one stage of lead did not cover.
 // They are separate LDS objects, always addressed with a compile-time
 // index, so the compiler can tell a slot being read from one with loads in
-// flight and does not wait for those. Four of them (A0, A1, B0, B1) also
-// stage the epilogue's C tile, the fifth holds its wave maxima. Declared
-// once for the file, so a kernel that runs tiles of two GEMM variants still
-// holds 160 KB.
+// flight and does not wait for those. B2 also stages the epilogue's C
+// quarters (8 KB per wave), and A0, A1, B0, B1 the tail fixup's C tile.
+// Declared once for the file, so a kernel that runs tiles of two GEMM
+// variants still holds 160 KB.
 __shared__ uint4 g_a0[kOpBytes / 16];
 __shared__ uint4 g_a1[kOpBytes / 16];
 __shared__ uint4 g_b0[kOpBytes / 16];
@@ -170,7 +162,7 @@ __device__ inline lds_u8* b_slot() {
   else if constexpr (S % 3 == 1) return (lds_u8*)g_b1;
   else return (lds_u8*)g_b2;
 }
-// 32 KB region j (0..3) of the epilogue's C staging: A0, A1, B0, B1
+// 32 KB region j (0..3) of the tail fixup's C staging: A0, A1, B0, B1
 __device__ inline lds_u8* c_region(int j) {
   return j == 0 ? (lds_u8*)g_a0 : j == 1 ? (lds_u8*)g_a1 : j == 2 ? (lds_u8*)g_b0 : (lds_u8*)g_b1;
 }
@@ -578,126 +570,100 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, fp8_sca
     return;
   }
 
-  // ---- epilogue: 2^s (exact power-of-two scaling), bf16 RNE, then the
-  // 256 x 256 bf16 tile (128 KB: 64 rows of 512 bytes per 32 KB region) is
-  // staged row-major in LDS so the block writes C in whole 512-byte rows of
-  // 16-byte stores. 16-byte chunks of each LDS row are XOR-swizzled by
-  // (row & 31). Region 2 wm + (mi >> 1) holds rows 64 (2 wm + (mi >> 1)) ..
-  // + 63. Two halves: blocks mi = 0, 1 are staged (regions 0 and 2), then
-  // those regions are written to C while blocks mi = 2, 3 are staged
-  // (regions 1 and 3), so the stores of the first half overlap the
-  // conversions of the second (measured 1-5 % faster on multi-wave
-  // GEMMs than staging the whole tile first).
-  u16x2 cmax = {0, 0};  // AMAX: running max of the 15-bit magnitudes written
-  auto stage = [&](auto MLO_) {
-    constexpr int MLO = decltype(MLO_)::value;
-#pragma unroll
-    for (int mi = MLO; mi < MLO + 2; ++mi) {
-      const int row = 128 * wm + 32 * mi + frow;
-      lds_u8* crow = c_region(2 * wm + (mi >> 1)) + (row & 63) * 512;
-#pragma unroll
-      for (int ni = 0; ni < 4; ++ni) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const f32x2 lo = {ldexpf(acc[mi][ni][4 * q + 0], shift), ldexpf(acc[mi][ni][4 * q + 1], shift)};
-          const f32x2 hi = {ldexpf(acc[mi][ni][4 * q + 2], shift), ldexpf(acc[mi][ni][4 * q + 3], shift)};
-          const uint32_t p0 = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2));
-          const uint32_t p1 = __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2));
-          const int chunk = 16 * wn + 4 * ni + q;
-          *(lds_u32x2*)(crow + ((chunk ^ (row & 31)) << 4) + 8 * g) = (u32x2){p0, p1};
-          if constexpr (AMAX) {
-            cmax = __builtin_elementwise_max(cmax, __builtin_bit_cast(u16x2, p0 & 0x7FFF7FFFu));
-            cmax = __builtin_elementwise_max(cmax, __builtin_bit_cast(u16x2, p1 & 0x7FFF7FFFu));
-          }
-        }
-        // one 32 x 32 block at a time, which bounds how many accumulators
-        // are moved out of the accumulation registers at once
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-  };
-
-  // Drain of region j: lane t takes 16-byte chunk c = t % 32 of rows
-  // r0 + 8k (r0 = t / 32, k = 0..7) of the region. The LDS swizzle of row
-  // 64j + r0 + 8k is r0 + 8 (k % 4), so four per-lane LDS offsets plus
-  // immediates address every read.
+  // ---- epilogue, each wave on its own: 2^s (exact power-of-two scaling),
+  // bf16 RNE, and the wave's 128 x 128 block of C written in four quarters
+  // of 32 rows (accumulator row block mi). A quarter (32 rows x 256 bytes)
+  // is staged row-major in the wave's own 8 KB of slot B2 and read back so
+  // that 16 lanes hold one 256-byte row piece: a store instruction then
+  // writes 4 rows x 256 bytes, whole cache lines (scattered 8-byte stores
+  // had made HBM writes 5x the output size). The staging area is private
+  // to the wave and one wave's LDS accesses are processed in order, so no
+  // workgroup barrier is needed; the stores of one quarter drain while the
+  // next is converted. 16-byte chunks of a staged row are XOR-swizzled by
+  // (row & 15), which spreads both the 8-byte writes (32 rows x one chunk
+  // per instruction) and the 16-byte reads over all banks.
+  lds_u8* const wst = (lds_u8*)g_b2 + 8192 * w;
   // (the thread index is passed through an empty asm so that none of this
   // address arithmetic is hoisted above the k-loop, where registers are full)
   int te = t;
   asm volatile("" : "+v"(te));
-  const int c = te & 31, r0 = te >> 5;
+  const int dl = te & 63, dc = dl & 15, dr = dl >> 4;  // read-back: chunk dc of rows dr + 4k
   int loff[4];
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) loff[kk] = (r0 + 8 * kk) * 512 + ((c ^ (r0 + 8 * kk)) << 4);
+  for (int kk = 0; kk < 4; ++kk) loff[kk] = (dr + 4 * kk) * 256 + ((dc ^ (dr + 4 * kk)) << 4);
+  const int wsw = te & 15;                                            // frow & 15
+  lds_u8* const wrow = wst + (te & 31) * 256 + 8 * ((te >> 5) & 1);  // row frow, half g
+  const int col = n0 + 128 * wn + 8 * dc;
+  const bool col_ok = col < N;
   const bool full_tile = m0 + kBM <= M && n0 + kBN <= N;
-  const bool col_ok = n0 + 8 * c < N;
-  uint16_t* const cbase = C + (int64_t)(m0 + r0) * N + n0 + 8 * c;
-  const int64_t step8 = (int64_t)8 * N;
-  auto drain = [&](const lds_u8* src, int j, auto FULL_) {
+  // AMAX: max of the 15-bit magnitudes written, per quarter in cmax, then
+  // reduced over the wave into the wave-uniform wmax
+  uint32_t wmax = 0;
+  auto quarter = [&](auto MI_, auto FULL_) {
+    constexpr int mi = decltype(MI_)::value;
     constexpr bool FULL = decltype(FULL_)::value;
+    u16x2 cmax = {0, 0};
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x2 lo = {ldexpf(acc[mi][ni][4 * q + 0], shift), ldexpf(acc[mi][ni][4 * q + 1], shift)};
+        const f32x2 hi = {ldexpf(acc[mi][ni][4 * q + 2], shift), ldexpf(acc[mi][ni][4 * q + 3], shift)};
+        const uint32_t p0 = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2));
+        const uint32_t p1 = __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2));
+        // lane (frow, g) holds columns 32 ni + 8 q + 4 g .. + 3 of row frow:
+        // half g of 16-byte chunk 4 ni + q
+        *(lds_u32x2*)(wrow + (((4 * ni + q) ^ wsw) << 4)) = (u32x2){p0, p1};
+        if constexpr (AMAX) {
+          cmax = __builtin_elementwise_max(cmax, __builtin_bit_cast(u16x2, p0 & 0x7FFF7FFFu));
+          cmax = __builtin_elementwise_max(cmax, __builtin_bit_cast(u16x2, p1 & 0x7FFF7FFFu));
+        }
+      }
+      // one 32 x 32 block at a time, which bounds how many accumulators
+      // are moved out of the accumulation registers at once
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (AMAX) {
+      uint32_t r = cmax.x > cmax.y ? cmax.x : cmax.y;
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) {
+        const uint32_t o = (uint32_t)__shfl_xor((int)r, off, 64);
+        r = o > r ? o : r;
+      }
+      r = __builtin_amdgcn_readfirstlane(r);
+      wmax = r > wmax ? r : wmax;
+    }
     u32x4 v[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) v[k] = *(const lds_u32x4*)(src + loff[k & 3] + (k >> 2) * 16384);
-    uint16_t* cp = cbase + (int64_t)(64 * j) * N;
+    for (int k = 0; k < 8; ++k) v[k] = *(const lds_u32x4*)(wst + loff[k & 3] + (k >> 2) * 4096);
+    const int row = m0 + 128 * wm + 32 * mi + dr;
+    uint16_t* cp = C + (int64_t)row * N + col;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      if (FULL || (col_ok && m0 + 64 * j + r0 + 8 * k < M)) *(u32x4*)cp = v[k];
-      cp += step8;
+      if (FULL || (col_ok && row + 4 * k < M)) *(u32x4*)cp = v[k];
+      cp += (int64_t)4 * N;
     }
   };
-  auto drain_pair = [&](const lds_u8* src_a, int ja, const lds_u8* src_b, int jb) {
-    if (full_tile) {
-      drain(src_a, ja, std::true_type{});
-      drain(src_b, jb, std::true_type{});
-    } else {
-      drain(src_a, ja, std::false_type{});
-      drain(src_b, jb, std::false_type{});
-    }
+  auto all_quarters = [&](auto FULL_) {
+    quarter(std::integral_constant<int, 0>{}, FULL_);
+    quarter(std::integral_constant<int, 1>{}, FULL_);
+    quarter(std::integral_constant<int, 2>{}, FULL_);
+    quarter(std::integral_constant<int, 3>{}, FULL_);
   };
-
-  using M0 = std::integral_constant<int, 0>;
-  using M2 = std::integral_constant<int, 2>;
-  stage(M0{});
+  if (full_tile) all_quarters(std::true_type{});
+  else all_quarters(std::false_type{});
   // AMAX: rows past M and columns past N repeat valid rows / columns
-  // (clamped operand rows), so the tile max is a max over real outputs.
-  // The first half's wave maximum is parked in LDS, so the running max is
-  // not live across the first half's stores.
-  auto wave_max = [&]() -> uint32_t {
-    uint32_t r = cmax.x > cmax.y ? cmax.x : cmax.y;
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      const uint32_t o = (uint32_t)__shfl_xor((int)r, off, 64);
-      r = o > r ? o : r;
-    }
-    return r;
-  };
-  uint32_t(*wmax)[kThreads / 64] = (uint32_t(*)[kThreads / 64])g_b2;  // the slot C staging leaves free
+  // (clamped operand rows), so the tile max is a max over real outputs;
+  // one merge per wave
   if constexpr (AMAX) {
-    const uint32_t r = wave_max();
-    if (lane == 0) wmax[0][w] = r;
-    cmax = (u16x2){0, 0};
-  }
-  block_sync_lds();
-  drain_pair(c_region(0), 0, c_region(2), 2);
-  stage(M2{});
-  if constexpr (AMAX) {
-    const uint32_t r = wave_max();
-    if (lane == 0) wmax[1][w] = r > wmax[0][w] ? r : wmax[0][w];
-  }
-  block_sync_lds();
-  if constexpr (AMAX) {
-    if (t == 0) {
-      uint32_t b = wmax[1][0];
-#pragma unroll
-      for (int i = 1; i < kThreads / 64; ++i) b = wmax[1][i] > b ? wmax[1][i] : b;
-      const unsigned long long v = (reduction_tag(s_out) << 16) | b;
+    if ((te & 63) == 0) {
+      const unsigned long long v = (reduction_tag(s_out) << 16) | wmax;
       unsigned long long* word = (unsigned long long*)&s_out->gen_max;
       const unsigned long long seen = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (v > seen) atomicMax(word, v);
-      if (tile == 0) s_out->sat_count = 0u;
     }
+    if (tile == 0 && te == 0) s_out->sat_count = 0u;
   }
-  drain_pair(c_region(1), 1, c_region(3), 3);
 }
 
 // One GEMM: one block per output tile.
