@@ -20,8 +20,8 @@
 //    the accumulation registers).
 //  * Operands stream through LDS in stages of k = 128 bytes (256 rows of A
 //    and of B, 32 KB each), held in two slots for A and three for B (160 KB),
-//    so B, the operand streamed from HBM, is loaded two stages ahead and A
-//    one. 128 bytes is one cache line per row: a 16-byte-per-lane load then
+//    so B, the operand streamed from HBM, is loaded a stage and a half
+//    ahead and A one. 128 bytes is one cache line per row: a 16-byte-per-lane load then
 //    covers 8 whole lines, which the load path handles markedly faster than
 //    16 half lines. Global memory is copied straight into LDS by buffer
 //    loads with the LDS-write form (no register staging).
@@ -135,8 +135,8 @@ struct GemmParams {
 
 // Stage buffers: two slots for A's part of a stage and three for B's
 // (32 KB each, 160 KB in all, the whole LDS of a CU), so B's loads are
-// issued a stage earlier than A's. B is the operand streamed from HBM on
-// the layer shapes (the weights in the forward and dgrad GEMMs, the
+// issued half a stage earlier than A's. B is the operand streamed from HBM
+// on the layer shapes (the weights in the forward and dgrad GEMMs, the
 // gradient in the wgrad), whose latency one stage of lead did not cover.
 // They are separate LDS objects, always addressed with a compile-time
 // index, so the compiler can tell a slot being read from one with loads in
@@ -424,18 +424,34 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, fp8_sca
         acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[ni], f.a[mi], acc[mi][ni], FB, FA,
                                                                        0, 0, 0, 0);
   };
+  // MFMAs lo .. hi-1 of a step (block i = 4 mi + ni)
+  auto mfma_part = [&](const Frags& f, auto LO_, auto HI_) {
+    constexpr int LO = decltype(LO_)::value, HI = decltype(HI_)::value;
+#pragma unroll
+    for (int i = LO; i < HI; ++i)
+      acc[i >> 2][i & 3] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[i & 3], f.a[i >> 2], acc[i >> 2][i & 3],
+                                                                          FB, FA, 0, 0, 0, 0);
+  };
+#ifndef EARLY_BAR
+#define EARLY_BAR 0
+#endif
 
   // Software pipeline. Stage s lives in A slot s % 2 and B slot s % 3; its
   // two MFMA steps use fr[0] (k-half 0) and fr[1] (k-half 1). On entry to
-  // stage s, fr[0] holds its first half, and the loads in flight are A of
-  // stage s+1, then B of stage s+2 (B of stage s+1 was issued a stage
-  // before them).
-  //  step 2s:   read k-half 1 of stage s into fr[1]; MFMAs on fr[0].
+  // stage s, fr[0] holds its first half, and the loads in flight are B of
+  // stage s+1, then A of stage s+1.
+  //  step 2s:   read k-half 1 of stage s into fr[1]; issue B of stage s+2
+  //             into the slot of stage s-1 (free since that stage's
+  //             barrier); MFMAs on fr[0].
   //  step 2s+1: wait for stage s+1 (own loads by vmcnt: all but the last
   //             8, which are B of stage s+2; everyone's by the barrier,
   //             which also follows every wave's reads of stage s); issue A
-  //             of stage s+2 and B of stage s+3 into the slots stage s
-  //             freed; read k-half 0 of stage s+1 into fr[0]; MFMAs on fr[1].
+  //             of stage s+2 into the A slot stage s freed; read k-half 0 of
+  //             stage s+1 into fr[0]; MFMAs on fr[1].
+  // Each step thus issues 8 of the stage's 16 loads: with all 16 in the
+  // second step, the load path was busy for that whole step and held up
+  // instruction issue (the step ran ~230 cycles over its 1024 of MFMAs; now
+  // ~20-70).
   Frags fr[2];
   {
     if (nk > 0) {
@@ -446,7 +462,6 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, fp8_sca
       issue_any(IsA{}, a_slot<1>(), 1);
       issue_any(IsB{}, b_slot<1>(), 1);
     }
-    if (nk > 2) issue_any(IsB{}, b_slot<2>(), 2);
     // the accumulators are zeroed here, while the first loads are in
     // flight: left to the compiler, the 256 writes sat between the wait for
     // stage 0 and the first MFMA (~0.5 us per tile)
@@ -455,8 +470,8 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, fp8_sca
 #pragma unroll
       for (int ni = 0; ni < 4; ++ni) asm volatile("" : "+a"(acc[mi][ni]));
     if (nk > 0) {
-      if (nfull >= 3) wait_vmcnt<24>();  // stages 1 and 2 full: their 24 loads may stay in flight
-      else wait_vmcnt<0>();              // a partial stage among them: count not exact
+      if (nfull >= 3) wait_vmcnt<16>();  // stage 1 full: its 16 loads may stay in flight
+      else wait_vmcnt<0>();              // a partial stage among the first ones: count not exact
       block_sync_lds();
       read_step(a_slot<0>(), b_slot<0>(), 0, fr[0]);
     }
@@ -468,35 +483,34 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, fp8_sca
   auto stage_main = [&](auto J_, int s) {
     constexpr int J = decltype(J_)::value;
     read_step(a_slot<J>(), b_slot<J>(), 1, fr[1]);
-    mfma_all(fr[0]);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, kReadsPer, 0);  // DS read
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    issue_b(b_slot<J + 2>(), s + 2);  // into the slot of stage s-1, free since its barrier
+    mfma_part(fr[0], std::integral_constant<int, 0>{}, std::integral_constant<int, 16 - EARLY_BAR>{});
+    static_for<16 - EARLY_BAR>([&](auto I_) {
+      constexpr int i = decltype(I_)::value;
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                         // MFMA
+      if constexpr (i < 8) __builtin_amdgcn_sched_group_barrier(0x100, kReadsPer, 0);  // DS read
+      if constexpr (i & 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);    // buffer load to LDS
+    });
     __builtin_amdgcn_sched_barrier(0);
     wait_vmcnt<8>();   // A of stage s+1 landed (and B of s+1, issued before it); B of s+2 may fly
     block_sync_lds();  // everyone's loads landed, everyone's reads of stage s's slots done
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (EARLY_BAR > 0) {
+      mfma_part(fr[0], std::integral_constant<int, 16 - EARLY_BAR>{}, std::integral_constant<int, 16>{});
+      __builtin_amdgcn_sched_barrier(0);
+    }
     issue_a(a_slot<J>(), s + 2);
-    issue_b(b_slot<J>(), s + 3);
     read_step(a_slot<J + 1>(), b_slot<J + 1>(), 0, fr[0]);
     mfma_all(fr[1]);
-    // one load per MFMA: in bursts of two per MFMA the four waves' loads
-    // outran the load path and stalled issue (measured 2-3 % slower)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, kReadsPer, 0);  // DS read
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);          // buffer load to LDS
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // buffer load to LDS
-    }
+    // one load per two MFMAs in either step: a stage's 64 KB of loads
+    // issued in one step kept the load path busy for the whole step and
+    // stalled instruction issue (that step ran ~230 cycles over its MFMAs)
+    static_for<16>([&](auto I_) {
+      constexpr int i = decltype(I_)::value;
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                         // MFMA
+      if constexpr (i < 8) __builtin_amdgcn_sched_group_barrier(0x100, kReadsPer, 0);  // DS read
+      if constexpr (i & 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);    // buffer load to LDS
+    });
     __builtin_amdgcn_sched_barrier(0);
   };
   // general stage (the last three when one of them is partial, or all of
@@ -509,12 +523,12 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, fp8_sca
     lds_u8* const as[2] = {a_slot<0>(), a_slot<1>()};
     lds_u8* const bs[3] = {b_slot<0>(), b_slot<1>(), b_slot<2>()};
     read_step(as[s & 1], bs[s % 3], 1, fr[1]);
+    if (s + 2 < nk) issue_any(IsB{}, bs[(s + 2) % 3], s + 2);
     mfma_all(fr[0]);
     if (s + 1 < nk) {
       wait_vmcnt<0>();
       block_sync_lds();
       if (s + 2 < nk) issue_any(IsA{}, as[s & 1], s + 2);
-      if (s + 3 < nk) issue_any(IsB{}, bs[s % 3], s + 3);
       read_step(as[(s + 1) & 1], bs[(s + 1) % 3], 0, fr[0]);
     }
     mfma_all(fr[1]);
