@@ -424,17 +424,6 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, fp8_sca
         acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[ni], f.a[mi], acc[mi][ni], FB, FA,
                                                                        0, 0, 0, 0);
   };
-  // MFMAs lo .. hi-1 of a step (block i = 4 mi + ni)
-  auto mfma_part = [&](const Frags& f, auto LO_, auto HI_) {
-    constexpr int LO = decltype(LO_)::value, HI = decltype(HI_)::value;
-#pragma unroll
-    for (int i = LO; i < HI; ++i)
-      acc[i >> 2][i & 3] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[i & 3], f.a[i >> 2], acc[i >> 2][i & 3],
-                                                                          FB, FA, 0, 0, 0, 0);
-  };
-#ifndef EARLY_BAR
-#define EARLY_BAR 0
-#endif
 
   // Software pipeline. Stage s lives in A slot s % 2 and B slot s % 3; its
   // two MFMA steps use fr[0] (k-half 0) and fr[1] (k-half 1). On entry to
@@ -484,8 +473,8 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, fp8_sca
     constexpr int J = decltype(J_)::value;
     read_step(a_slot<J>(), b_slot<J>(), 1, fr[1]);
     issue_b(b_slot<J + 2>(), s + 2);  // into the slot of stage s-1, free since its barrier
-    mfma_part(fr[0], std::integral_constant<int, 0>{}, std::integral_constant<int, 16 - EARLY_BAR>{});
-    static_for<16 - EARLY_BAR>([&](auto I_) {
+    mfma_all(fr[0]);
+    static_for<16>([&](auto I_) {
       constexpr int i = decltype(I_)::value;
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                         // MFMA
       if constexpr (i < 8) __builtin_amdgcn_sched_group_barrier(0x100, kReadsPer, 0);  // DS read
@@ -495,10 +484,6 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, fp8_sca
     wait_vmcnt<8>();   // A of stage s+1 landed (and B of s+1, issued before it); B of s+2 may fly
     block_sync_lds();  // everyone's loads landed, everyone's reads of stage s's slots done
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (EARLY_BAR > 0) {
-      mfma_part(fr[0], std::integral_constant<int, 16 - EARLY_BAR>{}, std::integral_constant<int, 16>{});
-      __builtin_amdgcn_sched_barrier(0);
-    }
     issue_a(a_slot<J>(), s + 2);
     read_step(a_slot<J + 1>(), b_slot<J + 1>(), 0, fr[0]);
     mfma_all(fr[1]);
