@@ -136,7 +136,11 @@ def test_record_reuse_with_shrinking_gradients():
                                              (128, 528, 1040, 2, 3)])
 def test_wgrad_fp8_row_major_operands(M, K, N, margin, mu):
     """The row-major FP8 copies X [M,K] and dY [M,N], read reduction-major,
-    give the transposed-copy result byte for byte (dW, E5M2 codes, record)."""
+    against the transposed copies read row-wise: the two run different tile
+    bodies of the GEMM (rounding FP32 partial sums at different k
+    boundaries), so each dW is held to the GEMM tolerance against the
+    oracle, and each call's record, E5M2 codes and clipped count are checked
+    bit for bit against the oracle applied to its own dW."""
     xb, dyb = _operands(M, K, N, M + 5 * K + 3 * N)
     x8t, sx, dy8t, sdy = _fp8_operands(xb, dyb, margin, mu)
     x8, _ = tsf.fp8_quantize(to_dev_bf16(xb), "e4m3", tsf.new_scale(1)[0], margin, 0, transposed=False)
@@ -144,12 +148,10 @@ def test_wgrad_fp8_row_major_operands(M, K, N, margin, mu):
     a = tsf.fp8_wgrad_fp8(x8t, sx, dy8t, sdy, margin, mu, transposed=True)
     b = tsf.fp8_wgrad_fp8(x8, sx, dy8, sdy, margin, mu, transposed=True, x_layout="cols", dy_layout="cols")
     torch.cuda.synchronize()
-    assert torch.equal(a[0].view(torch.int16), b[0].view(torch.int16))
-    assert torch.equal(a[1], b[1]) and torch.equal(a[2], b[2])
-    ra, rb = tsf.read_scale(a[3]), tsf.read_scale(b[3])
-    assert all(ra[k] == rb[k] for k in ("bias", "flags", "scale", "sat_count")) and \
-        f32_bits(ra["amax"]) == f32_bits(rb["amax"])
-    _check_chain(b[0], b[1], b[2], b[3], margin, mu)
+    bx, bdy = tsf.read_scale(sx)["bias"], tsf.read_scale(sdy)["bias"]
+    for dW, dw8, dw8t, s_dw in (a, b):
+        _check_dw_vs_oracle(dW, xb, dyb, bx, bdy)
+        _check_chain(dW, dw8, dw8t, s_dw, margin, mu)
 
 
 def test_wgrad_fp8_full_size_gpt7b_up():
