@@ -212,7 +212,8 @@ def mfma_markdown(d: str, command: str, layer: str = "GPT-175B-style layer") -> 
              "Command:", "", "```", command, "```", "",
              "flops = 512 x (SQ_INSTS_VALU_MFMA_MOPS_F8 + SQ_INSTS_VALU_MFMA_MOPS_F6F4); MFMA cycles = "
              "SQ_VALU_MFMA_BUSY_CYCLES per SIMD (1024 SIMDs), which the hardware counts as 64 per "
-             "32x32x64 FP8 MFMA, so it equals flops / (1024 x 2048) when no MFMA work is wasted; "
+             "32x32x64 and 32 per 16x16x128 FP8 MFMA (2048 flops per SIMD cycle either way), so it "
+             "equals flops / (1024 x 2048) when no MFMA work is wasted; "
              "clock = SQ_BUSY_CYCLES per shader engine (32 of them) / dispatch duration (waves are "
              "present for the whole GEMM); MFMA busy = MFMA cycles / (clock x duration); peak at "
              "clock = 256 CUs x 8192 FP8 flops per clock x clock. Kernels run one at a time under "
