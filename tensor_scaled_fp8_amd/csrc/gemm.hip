@@ -994,7 +994,6 @@ __device__ __forceinline__ void gemm_tile16(const GemmParams& p, int tile, fp8_s
     });
     __builtin_amdgcn_sched_barrier(0);
   };
-  using I0c = std::integral_constant<int, 0>;
   using I1c = std::integral_constant<int, 1>;
   using I2c = std::integral_constant<int, 2>;
   using I4c = std::integral_constant<int, 4>;

@@ -154,6 +154,30 @@ def test_wgrad_fp8_row_major_operands(M, K, N, margin, mu):
         _check_chain(dW, dw8, dw8t, s_dw, margin, mu)
 
 
+@pytest.mark.parametrize("M,K,N", [(400, 272, 528), (784, 2064, 272)])
+@pytest.mark.parametrize("x_layout,dy_layout", [("rows", "cols"), ("cols", "rows")])
+def test_wgrad_fp8_mixed_layouts(M, K, N, x_layout, dy_layout):
+    """One operand as its transposed copy (read row-wise), the other as the
+    row-major copy (read reduction-major): dW within the GEMM tolerance of
+    the oracle, and the record, E5M2 codes and clipped count bit-exact
+    against the oracle applied to the kernel's own dW. (rows, cols) is the
+    fused-amax layout that runs on the 32 x 32 x 64 tile body although its
+    A is row-layout."""
+    margin, mu = 0, 1
+    xb, dyb = _operands(M, K, N, 7 * M + K + N + (x_layout == "rows"))
+    x8t, sx, dy8t, sdy = _fp8_operands(xb, dyb, margin, mu)
+    x8, _ = tsf.fp8_quantize(to_dev_bf16(xb), "e4m3", tsf.new_scale(1)[0], margin, 0, transposed=False)
+    dy8, _ = tsf.fp8_quantize(to_dev_bf16(dyb), "e5m2", tsf.new_scale(1)[0], margin, mu, transposed=False)
+    xo = x8t if x_layout == "rows" else x8
+    dyo = dy8t if dy_layout == "rows" else dy8
+    dW, dw8, dw8t, s_dw = tsf.fp8_wgrad_fp8(xo, sx, dyo, sdy, margin, mu, transposed=True, x_layout=x_layout,
+                                            dy_layout=dy_layout)
+    torch.cuda.synchronize()
+    bx, bdy = tsf.read_scale(sx)["bias"], tsf.read_scale(sdy)["bias"]
+    _check_dw_vs_oracle(dW, xb, dyb, bx, bdy)
+    _check_chain(dW, dw8, dw8t, s_dw, margin, mu)
+
+
 def test_wgrad_fp8_full_size_gpt7b_up():
     """Full size (dW 4096 x 16384 from 4096 tokens), from the training
     step's row-major FP8 copies: record and every E5M2 byte bit-exact vs the
