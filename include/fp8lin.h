@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define FP8LIN_ABI_VERSION 12
+#define FP8LIN_ABI_VERSION 13
 
 typedef enum fp8_fmt {
   FP8_E4M3 = 0, /* OCP E4M3FN: weights and activations [AMAX bullet 4] */
@@ -505,6 +505,30 @@ fp8_status fp8_adam_init_master(int64_t n, const void* w_bf16, uint16_t* w16, fp
 fp8_status fp8_adam_step(int64_t n, const uint8_t* g8, const fp8_scale_t* s_g, uint8_t* m1, fp8_scale_t* s_m1,
                          uint16_t* m2, fp8_scale_t* s_m2, uint16_t* w16, fp8_scale_t* s_w, void* w_bf16, float lr,
                          float beta1, float beta2, float eps, float weight_decay, int32_t step, hipStream_t stream);
+
+/*
+ * fp8_adam_step_spec: the step of fp8_adam_step [FP8LM "Proposed method",
+ * O2, as above] in one pass over the state in the common case, out of
+ * place: reads g8, m1, m2, w16 and writes the new state to m1_out, m2_out,
+ * w16_out (and the bf16 weights to w_bf16 if not NULL), encoded with the
+ * scales the records hold now while the new maxima are taken; a second
+ * kernel derives the new scales and, only where one differs from its
+ * record's, recomputes every element from the untouched inputs with the
+ * new scales. The records are then rewritten as by fp8_adam_step, and the
+ * outputs and records equal fp8_adam_step's on the same inputs bit for bit.
+ * HBM traffic 13 bytes per parameter (6 read, 7 written) when no scale
+ * changes, 24 when one does.
+ *   Arguments as fp8_adam_step; m1_out [n] u8, m2_out and w16_out [n] fp16
+ *   bits, 16-B aligned, none overlapping an input or another output
+ *   (else FP8_ERR_INVALID). missed: NULL or a device uint32, 4-B aligned,
+ *   set to a bit mask of the records whose bias changed (bit 0 m1, bit 1
+ *   m2, bit 2 w), i.e. the steps that took the second pass.
+ */
+fp8_status fp8_adam_step_spec(int64_t n, const uint8_t* g8, const fp8_scale_t* s_g, const uint8_t* m1,
+                              const uint16_t* m2, const uint16_t* w16, uint8_t* m1_out, uint16_t* m2_out,
+                              uint16_t* w16_out, fp8_scale_t* s_m1, fp8_scale_t* s_m2, fp8_scale_t* s_w,
+                              void* w_bf16, uint32_t* missed, float lr, float beta1, float beta2, float eps,
+                              float weight_decay, int32_t step, hipStream_t stream);
 
 /* How fp8_linear_fwd_cached scales X. */
 typedef enum fp8_scaling {

@@ -45,6 +45,9 @@ SIGNATURES = {
     "fp8_adam_init_master": (c_int, [c_i64, c_vp, c_vp, c_vp, c_vp]),
     "fp8_adam_step": (c_int, [c_i64, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, ctypes.c_float,
                               ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_int32, c_vp]),
+    "fp8_adam_step_spec": (c_int, [c_i64, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                   c_vp, ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_float,
+                                   ctypes.c_float, ctypes.c_int32, c_vp]),
 }
 
 FP8_E4M3, FP8_E5M2 = 0, 1
@@ -53,7 +56,7 @@ FP8_OK, FP8_ERR_INVALID, FP8_ERR_UNSUPPORTED, FP8_ERR_HIP = 0, 1, 2, 3
 FLAG_NONFINITE, FLAG_ZERO, FLAG_CLAMPED = 1, 2, 4
 FP8_SCALING_AMAX, FP8_SCALING_FIXED = 0, 1
 FP8_SPLIT_AUTO, FP8_SPLIT_NEVER, FP8_SPLIT_TAIL = 0, 1, 2
-ABI_VERSION = 12
+ABI_VERSION = 13
 FP8_NOALLOC_SCRATCH_BYTES = 128 * 2 * 65536 * 4   # the device scratch of fp8_gemm_noalloc
 
 

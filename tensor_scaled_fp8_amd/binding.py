@@ -539,6 +539,7 @@ class AdamState:
         self.scales = new_scale(3, dev)
         self.s_m1, self.s_m2, self.s_w = self.scales[0], self.scales[1], self.scales[2]
         self.step_count = 0
+        self.alt = None     # second buffer set of fp8_adam_step_spec (out of place), made on first use
         fp8_adam_init_master(W.reshape(-1).contiguous(), self.w16, self.s_w)
 
 
@@ -563,5 +564,36 @@ def fp8_adam_step(state: AdamState, g8: torch.Tensor, s_g: torch.Tensor, lr: flo
                                _dev(state.w16, torch.int16, "w16"), _dev(state.s_w, torch.int32, "s_w"),
                                _dev(w_bf16, torch.bfloat16, "w_bf16"), lr, beta1, beta2, eps, weight_decay, t,
                                _stream(g8)), "fp8_adam_step")
+    state.step_count = t
+    return w_bf16
+
+
+def fp8_adam_step_spec(state: AdamState, g8: torch.Tensor, s_g: torch.Tensor, lr: float, beta1: float = 0.9,
+                       beta2: float = 0.95, eps: float = 1e-8, weight_decay: float = 0.0,
+                       w_bf16: Optional[torch.Tensor] = None, step: Optional[int] = None,
+                       missed: Optional[torch.Tensor] = None) -> Optional[torch.Tensor]:
+    """fp8_adam_step's step in one pass over the state when no scale changes
+    (fp8_adam_step_spec): the new state goes to the state's second buffer
+    set (made on first use), which then becomes the current one. missed: an
+    optional device int32 tensor of one element that receives the bit mask
+    of the records whose scale changed (bit 0 m1, 1 m2, 2 w)."""
+    if g8.numel() != state.n:
+        raise ValueError("gradient size differs from the state's")
+    if missed is not None and (missed.numel() < 1 or missed.dtype != torch.int32):
+        raise ValueError("missed must be an int32 tensor of at least one element")
+    t = state.step_count + 1 if step is None else int(step)
+    if state.alt is None:
+        state.alt = (torch.empty_like(state.m1), torch.empty_like(state.m2), torch.empty_like(state.w16))
+    m1o, m2o, w16o = state.alt
+    check(load().fp8_adam_step_spec(state.n, _dev(g8, torch.uint8, "g8"), _dev(s_g, torch.int32, "s_g"),
+                                    _dev(state.m1, torch.uint8, "m1"), _dev(state.m2, torch.int16, "m2"),
+                                    _dev(state.w16, torch.int16, "w16"), _dev(m1o, torch.uint8, "m1_out"),
+                                    _dev(m2o, torch.int16, "m2_out"), _dev(w16o, torch.int16, "w16_out"),
+                                    _dev(state.s_m1, torch.int32, "s_m1"), _dev(state.s_m2, torch.int32, "s_m2"),
+                                    _dev(state.s_w, torch.int32, "s_w"), _dev(w_bf16, torch.bfloat16, "w_bf16"),
+                                    _dev(missed, torch.int32, "missed"), lr, beta1, beta2, eps, weight_decay, t,
+                                    _stream(g8)), "fp8_adam_step_spec")
+    state.alt = (state.m1, state.m2, state.w16)
+    state.m1, state.m2, state.w16 = m1o, m2o, w16o
     state.step_count = t
     return w_bf16

@@ -26,6 +26,17 @@
 //     reduce_bits back to 0 for the next step.
 // HBM traffic per parameter: 6 bytes read twice, 5 written (+2 for the bf16
 // copy of the weights for the next forward).
+//
+// One-pass variant (launch_adam_spec), out of place: a new scale is almost
+// always the one the record already holds (a tensor's max moves across a
+// power of two only now and then), so the first kernel encodes with the
+// records' current scales while it takes the maxima, writing the new state
+// to separate buffers (6 bytes read, 5 + 2 written). The second kernel
+// derives the new scales; where all three equal the current ones it
+// returns at once, else it recomputes every element from the untouched
+// inputs with the new scales. Either way the stored state is bit for bit
+// what the two-pass step stores, since both encode the same fp32 values
+// with the same scale.
 #include "fp8lin_internal.h"
 
 namespace fp8lin {
@@ -105,6 +116,46 @@ __device__ inline void update8(u32x2 gw, u32x2 m1w, u32x4 m2w, u32x4 ww, float g
 
 __device__ inline uint32_t fbits(float x) { return __builtin_bit_cast(uint32_t, x); }
 
+// the 8 updated elements of vector i encoded with the scales sc1 (m1,
+// E4M3, saturating), sc2 (m2, FP16) and scw (w, FP16) and stored; the bf16
+// copy of w too when w_bf16 is not null
+__device__ inline void store8(const Vals v[kVec], float sc1, float sc2, float scw, int64_t i, u32x2* m1, u32x4* m2,
+                              u32x4* w, u32x4* w_bf16) {
+  uint32_t q[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    float f[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) f[k] = fminf(fmaxf(v[4 * j + k].m1 * sc1, -448.0f), 448.0f);
+    int r = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
+    r = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], r, true);
+    q[j] = (uint32_t)r;
+  }
+  m1[i] = (u32x2){q[0], q[1]};
+  uint32_t a[4], b[4], c[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    a[j] = enc_f16x2(v[2 * j].m2 * sc2, v[2 * j + 1].m2 * sc2);
+    b[j] = enc_f16x2(v[2 * j].w * scw, v[2 * j + 1].w * scw);
+    const f32x2 p = {v[2 * j].w, v[2 * j + 1].w};
+    c[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(p, bf16x2));
+  }
+  m2[i] = (u32x4){a[0], a[1], a[2], a[3]};
+  w[i] = (u32x4){b[0], b[1], b[2], b[3]};
+  if (w_bf16) w_bf16[i] = (u32x4){c[0], c[1], c[2], c[3]};
+}
+
+// the biases the step's new maxima give (m1: E4M3 rule, m2 and w: FP16
+// rule), from the records' reduce_bits merged by the first pass
+__device__ inline void new_biases(fp8_scale_t* s_m1, fp8_scale_t* s_m2, fp8_scale_t* s_w, int32_t b[3]) {
+  b[0] = bias_from_amax_bits(__hip_atomic_load(&s_m1->reduce_bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                             FP8_E4M3, 0, 0, nullptr);
+  b[1] = bias_fp16_from_amax_bits(__hip_atomic_load(&s_m2->reduce_bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                                  nullptr);
+  b[2] = bias_fp16_from_amax_bits(__hip_atomic_load(&s_w->reduce_bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                                  nullptr);
+}
+
 __device__ inline void block_merge_max(uint32_t v, uint32_t* target, uint32_t* lds) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
@@ -159,49 +210,87 @@ __global__ __launch_bounds__(kThreads) void adam_pass2_kernel(int64_t nvec, cons
                                                               AdamHyper h) {
   const float g_inv = s_g->scale_inv, m1_inv = s_m1->scale_inv, m2_inv = s_m2->scale_inv,
               w_inv = s_w->scale_inv;
-  auto new_scale = [](uint32_t* word, bool e4m3) {
-    const uint32_t mag = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const int32_t b = e4m3 ? bias_from_amax_bits(mag, FP8_E4M3, 0, 0, nullptr) : bias_fp16_from_amax_bits(mag, nullptr);
-    return pow2f(b);
-  };
-  const float sc1 = new_scale(&s_m1->reduce_bits, true), sc2 = new_scale(&s_m2->reduce_bits, false),
-              scw = new_scale(&s_w->reduce_bits, false);
+  int32_t b[3];
+  new_biases(s_m1, s_m2, s_w, b);
+  const float sc1 = pow2f(b[0]), sc2 = pow2f(b[1]), scw = pow2f(b[2]);
   for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nvec; i += (int64_t)gridDim.x * kThreads) {
     Vals v[kVec];
     update8(g8[i], m1[i], m2[i], w[i], g_inv, m1_inv, m2_inv, w_inv, h, v);
-    uint32_t q[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      float f[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) f[k] = fminf(fmaxf(v[4 * j + k].m1 * sc1, -448.0f), 448.0f);
-      int r = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
-      r = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], r, true);
-      q[j] = (uint32_t)r;
-    }
-    m1[i] = (u32x2){q[0], q[1]};
-    uint32_t a[4], b[4], c[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      a[j] = enc_f16x2(v[2 * j].m2 * sc2, v[2 * j + 1].m2 * sc2);
-      b[j] = enc_f16x2(v[2 * j].w * scw, v[2 * j + 1].w * scw);
-      const f32x2 p = {v[2 * j].w, v[2 * j + 1].w};
-      c[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(p, bf16x2));
-    }
-    m2[i] = (u32x4){a[0], a[1], a[2], a[3]};
-    w[i] = (u32x4){b[0], b[1], b[2], b[3]};
-    if (w_bf16) w_bf16[i] = (u32x4){c[0], c[1], c[2], c[3]};
+    store8(v, sc1, sc2, scw, i, m1, m2, w, w_bf16);
   }
 }
 
-__global__ void adam_publish_kernel(fp8_scale_t* s_m1, fp8_scale_t* s_m2, fp8_scale_t* s_w) {
+// One-pass variant, first kernel: the update of every element from the
+// inputs, its maxima merged as in pass 1, and the new state encoded with
+// the scales the records hold now (2^bias: a zeroed record's scale field
+// reads 0, its bias 0) into the output buffers.
+__global__ __launch_bounds__(kThreads) void adam_spec_kernel(int64_t nvec, const u32x2* __restrict__ g8,
+                                                             const fp8_scale_t* __restrict__ s_g,
+                                                             const u32x2* __restrict__ m1, const u32x4* __restrict__ m2,
+                                                             const u32x4* __restrict__ w, u32x2* __restrict__ m1o,
+                                                             u32x4* __restrict__ m2o, u32x4* __restrict__ wo,
+                                                             fp8_scale_t* s_m1, fp8_scale_t* s_m2, fp8_scale_t* s_w,
+                                                             u32x4* __restrict__ w_bf16, AdamHyper h) {
+  const float g_inv = s_g->scale_inv, m1_inv = s_m1->scale_inv, m2_inv = s_m2->scale_inv,
+              w_inv = s_w->scale_inv;
+  const float sc1 = pow2f(s_m1->bias), sc2 = pow2f(s_m2->bias), scw = pow2f(s_w->bias);
+  uint32_t x1 = 0, x2 = 0, xw = 0;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nvec; i += (int64_t)gridDim.x * kThreads) {
+    Vals v[kVec];
+    update8(__builtin_nontemporal_load(g8 + i), __builtin_nontemporal_load(m1 + i),
+            __builtin_nontemporal_load(m2 + i), __builtin_nontemporal_load(w + i), g_inv, m1_inv, m2_inv,
+            w_inv, h, v);
+#pragma unroll
+    for (int k = 0; k < kVec; ++k) {
+      const uint32_t a = fbits(v[k].m1) & 0x7FFFFFFFu, b = fbits(v[k].m2) & 0x7FFFFFFFu,
+                     c = fbits(v[k].w) & 0x7FFFFFFFu;
+      x1 = a > x1 ? a : x1;
+      x2 = b > x2 ? b : x2;
+      xw = c > xw ? c : xw;
+    }
+    store8(v, sc1, sc2, scw, i, m1o, m2o, wo, w_bf16);
+  }
+  __shared__ uint32_t lds[kThreads / 64];
+  block_merge_max(x1, &s_m1->reduce_bits, lds);
+  block_merge_max(x2, &s_m2->reduce_bits, lds);
+  block_merge_max(xw, &s_w->reduce_bits, lds);
+}
+
+// One-pass variant, second kernel: nothing to do when every new bias equals
+// its record's (the common case: each block sees that and returns); else
+// the whole update again from the untouched inputs, encoded with the new
+// scales (the bf16 weights, the same fp32 values, were written already).
+__global__ __launch_bounds__(kThreads) void adam_fix_kernel(int64_t nvec, const u32x2* __restrict__ g8,
+                                                            const fp8_scale_t* __restrict__ s_g,
+                                                            const u32x2* __restrict__ m1, const u32x4* __restrict__ m2,
+                                                            const u32x4* __restrict__ w, u32x2* __restrict__ m1o,
+                                                            u32x4* __restrict__ m2o, u32x4* __restrict__ wo,
+                                                            fp8_scale_t* s_m1, fp8_scale_t* s_m2, fp8_scale_t* s_w,
+                                                            AdamHyper h) {
+  int32_t b[3];
+  new_biases(s_m1, s_m2, s_w, b);
+  if (b[0] == s_m1->bias && b[1] == s_m2->bias && b[2] == s_w->bias) return;
+  const float g_inv = s_g->scale_inv, m1_inv = s_m1->scale_inv, m2_inv = s_m2->scale_inv,
+              w_inv = s_w->scale_inv;
+  const float sc1 = pow2f(b[0]), sc2 = pow2f(b[1]), scw = pow2f(b[2]);
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nvec; i += (int64_t)gridDim.x * kThreads) {
+    Vals v[kVec];
+    update8(g8[i], m1[i], m2[i], w[i], g_inv, m1_inv, m2_inv, w_inv, h, v);
+    store8(v, sc1, sc2, scw, i, m1o, m2o, wo, nullptr);
+  }
+}
+
+// missed (or null): bit i set where record i (m1, m2, w) changed its bias
+__global__ void adam_publish_kernel(fp8_scale_t* s_m1, fp8_scale_t* s_m2, fp8_scale_t* s_w, uint32_t* missed) {
   fp8_scale_t* recs[3] = {s_m1, s_m2, s_w};
+  uint32_t changed = 0;
 #pragma unroll
   for (int i = 0; i < 3; ++i) {
     fp8_scale_t* s = recs[i];
     const uint32_t mag = s->reduce_bits;
     uint32_t flags;
     const int32_t b = i == 0 ? bias_from_amax_bits(mag, FP8_E4M3, 0, 0, &flags) : bias_fp16_from_amax_bits(mag, &flags);
+    if (b != s->bias) changed |= 1u << i;
     s->amax = __builtin_bit_cast(float, mag);
     s->bias = b;
     s->scale = pow2f(b);
@@ -209,6 +298,7 @@ __global__ void adam_publish_kernel(fp8_scale_t* s_m1, fp8_scale_t* s_m2, fp8_sc
     s->flags = flags;
     s->reduce_bits = 0u;
   }
+  if (missed) *missed = changed;
 }
 
 // master-weight initialisation: bf16 weights -> FP16 with a per-tensor scale
@@ -290,7 +380,27 @@ hipError_t launch_adam(int64_t n, const uint8_t* g8, const fp8_scale_t* s_g, uin
                      (u32x2*)m1, s_m1, (u32x4*)m2, s_m2, (u32x4*)w, s_w, (u32x4*)w_bf16, h);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(adam_publish_kernel, dim3(1), dim3(1), 0, st, s_m1, s_m2, s_w);
+  hipLaunchKernelGGL(adam_publish_kernel, dim3(1), dim3(1), 0, st, s_m1, s_m2, s_w, (uint32_t*)nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_adam_spec(int64_t n, const uint8_t* g8, const fp8_scale_t* s_g, const uint8_t* m1,
+                            const uint16_t* m2, const uint16_t* w, uint8_t* m1_out, uint16_t* m2_out, uint16_t* w_out,
+                            fp8_scale_t* s_m1, fp8_scale_t* s_m2, fp8_scale_t* s_w, uint16_t* w_bf16,
+                            uint32_t* missed, const AdamHyper& h, hipStream_t st) {
+  const int64_t nvec = n / kVec;
+  const int64_t blocks = grid_for(nvec);
+  hipLaunchKernelGGL(adam_spec_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, st, nvec, (const u32x2*)g8, s_g,
+                     (const u32x2*)m1, (const u32x4*)m2, (const u32x4*)w, (u32x2*)m1_out, (u32x4*)m2_out,
+                     (u32x4*)w_out, s_m1, s_m2, s_w, (u32x4*)w_bf16, h);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(adam_fix_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, st, nvec, (const u32x2*)g8, s_g,
+                     (const u32x2*)m1, (const u32x4*)m2, (const u32x4*)w, (u32x2*)m1_out, (u32x4*)m2_out,
+                     (u32x4*)w_out, s_m1, s_m2, s_w, h);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(adam_publish_kernel, dim3(1), dim3(1), 0, st, s_m1, s_m2, s_w, missed);
   return hipGetLastError();
 }
 

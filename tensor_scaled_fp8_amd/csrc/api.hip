@@ -21,6 +21,48 @@ inline bool gemm_fits(int64_t M, int64_t N, int64_t R) {
   return M * R < kMaxOperandBytes && N * R < kMaxOperandBytes;
 }
 
+inline bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+
+// the checks fp8_adam_step and fp8_adam_step_spec share; fills h
+fp8_status adam_check(int64_t n, const uint8_t* g8, const fp8_scale_t* s_g, const void* m1, const fp8_scale_t* s_m1,
+                      const void* m2, const fp8_scale_t* s_m2, const void* w16, const fp8_scale_t* s_w,
+                      const void* w_bf16, float lr, float beta1, float beta2, float eps, float weight_decay,
+                      int32_t step, AdamHyper& h) {
+  if (n < 0 || step < 1) return FP8_ERR_INVALID;
+  const fp8_scale_t* recs[] = {s_g, s_m1, s_m2, s_w};
+  for (const fp8_scale_t* r : recs)
+    if (!r || !aligned16(r)) return FP8_ERR_INVALID;
+  if (!std::isfinite(lr) || !std::isfinite(eps) || !(eps > 0.0f) || !std::isfinite(weight_decay) ||
+      !(weight_decay >= 0.0f) || !(beta1 >= 0.0f && beta1 < 1.0f) || !(beta2 >= 0.0f && beta2 < 1.0f))
+    return FP8_ERR_INVALID;
+  if (n % 16) return FP8_ERR_UNSUPPORTED;
+  if (n > 0) {
+    const void* p[] = {g8, m1, m2, w16};
+    for (const void* q : p)
+      if (!q || !aligned16(q)) return FP8_ERR_INVALID;
+    if (w_bf16 && !aligned16(w_bf16)) return FP8_ERR_INVALID;
+  }
+  h.lr = lr;
+  h.beta1 = beta1;
+  h.beta2 = beta2;
+  h.eps = eps;
+  h.weight_decay = weight_decay;
+  h.bc1 = (float)(1.0 / (1.0 - std::pow((double)beta1, (double)step)));
+  h.bc2 = (float)(1.0 / (1.0 - std::pow((double)beta2, (double)step)));
+  return FP8_OK;
+}
+
+// a device byte range; two ranges overlap when both are non-empty and meet
+struct Range {
+  const void* p;
+  size_t bytes;
+};
+inline bool overlaps(const Range& a, const Range& b) {
+  if (!a.p || !b.p || a.bytes == 0 || b.bytes == 0) return false;
+  const uintptr_t a0 = (uintptr_t)a.p, b0 = (uintptr_t)b.p;
+  return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
 }  // namespace
 
 extern "C" {
@@ -337,29 +379,39 @@ fp8_status fp8_adam_init_master(int64_t n, const void* w_bf16, uint16_t* w16, fp
 fp8_status fp8_adam_step(int64_t n, const uint8_t* g8, const fp8_scale_t* s_g, uint8_t* m1, fp8_scale_t* s_m1,
                          uint16_t* m2, fp8_scale_t* s_m2, uint16_t* w16, fp8_scale_t* s_w, void* w_bf16, float lr,
                          float beta1, float beta2, float eps, float weight_decay, int32_t step, hipStream_t stream) {
-  if (n < 0 || step < 1) return FP8_ERR_INVALID;
-  const fp8_scale_t* recs[] = {s_g, s_m1, s_m2, s_w};
-  for (const fp8_scale_t* r : recs)
-    if (!r || !aligned16(r)) return FP8_ERR_INVALID;
-  if (!std::isfinite(lr) || !std::isfinite(eps) || !(eps > 0.0f) || !std::isfinite(weight_decay) ||
-      !(weight_decay >= 0.0f) || !(beta1 >= 0.0f && beta1 < 1.0f) || !(beta2 >= 0.0f && beta2 < 1.0f))
-    return FP8_ERR_INVALID;
-  if (n % 16) return FP8_ERR_UNSUPPORTED;
-  if (n > 0) {
-    const void* p[] = {g8, m1, m2, w16};
-    for (const void* q : p)
-      if (!q || !aligned16(q)) return FP8_ERR_INVALID;
-    if (w_bf16 && !aligned16(w_bf16)) return FP8_ERR_INVALID;
-  }
   AdamHyper h;
-  h.lr = lr;
-  h.beta1 = beta1;
-  h.beta2 = beta2;
-  h.eps = eps;
-  h.weight_decay = weight_decay;
-  h.bc1 = (float)(1.0 / (1.0 - std::pow((double)beta1, (double)step)));
-  h.bc2 = (float)(1.0 / (1.0 - std::pow((double)beta2, (double)step)));
+  const fp8_status st = adam_check(n, g8, s_g, m1, s_m1, m2, s_m2, w16, s_w, w_bf16, lr, beta1, beta2, eps,
+                                   weight_decay, step, h);
+  if (st != FP8_OK) return st;
   return hip_status(launch_adam(n, g8, s_g, m1, s_m1, m2, s_m2, w16, s_w, (uint16_t*)w_bf16, h, stream));
+}
+
+fp8_status fp8_adam_step_spec(int64_t n, const uint8_t* g8, const fp8_scale_t* s_g, const uint8_t* m1,
+                              const uint16_t* m2, const uint16_t* w16, uint8_t* m1_out, uint16_t* m2_out,
+                              uint16_t* w16_out, fp8_scale_t* s_m1, fp8_scale_t* s_m2, fp8_scale_t* s_w,
+                              void* w_bf16, uint32_t* missed, float lr, float beta1, float beta2, float eps,
+                              float weight_decay, int32_t step, hipStream_t stream) {
+  AdamHyper h;
+  const fp8_status st = adam_check(n, g8, s_g, m1, s_m1, m2, s_m2, w16, s_w, w_bf16, lr, beta1, beta2, eps,
+                                   weight_decay, step, h);
+  if (st != FP8_OK) return st;
+  if (missed && !aligned4(missed)) return FP8_ERR_INVALID;
+  if (n > 0) {
+    // outputs: present, aligned, and disjoint from every input and from each other
+    const Range outs[] = {{m1_out, (size_t)n}, {m2_out, 2 * (size_t)n}, {w16_out, 2 * (size_t)n},
+                          {w_bf16, w_bf16 ? 2 * (size_t)n : 0}};
+    const Range ins[] = {{g8, (size_t)n}, {m1, (size_t)n}, {m2, 2 * (size_t)n}, {w16, 2 * (size_t)n}};
+    for (int i = 0; i < 3; ++i)
+      if (!outs[i].p || !aligned16(outs[i].p)) return FP8_ERR_INVALID;
+    for (const Range& o : outs) {
+      for (const Range& q : ins)
+        if (overlaps(o, q)) return FP8_ERR_INVALID;
+      for (const Range& q : outs)
+        if (&q != &o && overlaps(o, q)) return FP8_ERR_INVALID;
+    }
+  }
+  return hip_status(launch_adam_spec(n, g8, s_g, m1, m2, w16, m1_out, m2_out, w16_out, s_m1, s_m2, s_w,
+                                     (uint16_t*)w_bf16, missed, h, stream));
 }
 
 }  // extern "C"

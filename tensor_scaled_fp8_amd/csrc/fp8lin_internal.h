@@ -197,6 +197,10 @@ struct AdamHyper {
 hipError_t launch_adam(int64_t n, const uint8_t* g8, const fp8_scale_t* s_g, uint8_t* m1, fp8_scale_t* s_m1,
                        uint16_t* m2, fp8_scale_t* s_m2, uint16_t* w, fp8_scale_t* s_w, uint16_t* w_bf16,
                        const AdamHyper& h, hipStream_t st);
+hipError_t launch_adam_spec(int64_t n, const uint8_t* g8, const fp8_scale_t* s_g, const uint8_t* m1,
+                            const uint16_t* m2, const uint16_t* w, uint8_t* m1_out, uint16_t* m2_out, uint16_t* w_out,
+                            fp8_scale_t* s_m1, fp8_scale_t* s_m2, fp8_scale_t* s_w, uint16_t* w_bf16,
+                            uint32_t* missed, const AdamHyper& h, hipStream_t st);
 hipError_t launch_master_init(int64_t n, const uint16_t* w_bf16, uint16_t* w, fp8_scale_t* s_w, hipStream_t st);
 
 }  // namespace fp8lin

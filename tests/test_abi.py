@@ -31,7 +31,7 @@ def test_header_functions_all_exported():
     for n in names:
         assert hasattr(lib, n), n
         assert n in _lib.SIGNATURES, f"binding lacks {n}"
-    assert lib.fp8_abi_version() == 12
+    assert lib.fp8_abi_version() == 13
 
 
 def test_status_strings():
@@ -247,6 +247,29 @@ def test_argument_validation_without_launch():
     assert ad(*aargs(s_m2=None)) == INV
     assert ad(*aargs(m1=_vp(ok + 8))) == INV
     assert ad(*aargs(wb=_vp(ok + 2))) == INV
+    # one-pass Adam (out of place): the same checks, plus the outputs
+    # present, aligned and disjoint from the inputs and from each other
+    sp = lib.fp8_adam_step_spec
+    base = {"g8": 0, "m1": 0x1000, "m2": 0x2000, "w": 0x3000, "m1o": 0x4000, "m2o": 0x5000, "wo": 0x6000,
+            "wb": 0x7000}
+    sargs = lambda **kw: [kw.get(k, d) for k, d in (
+        ("n", 64), ("g8", _vp(ok + base["g8"])), ("s_g", _vp(ok)), ("m1", _vp(ok + base["m1"])),
+        ("m2", _vp(ok + base["m2"])), ("w", _vp(ok + base["w"])), ("m1o", _vp(ok + base["m1o"])),
+        ("m2o", _vp(ok + base["m2o"])), ("wo", _vp(ok + base["wo"])), ("s_m1", _vp(ok)), ("s_m2", _vp(ok)),
+        ("s_w", _vp(ok)), ("wb", None), ("missed", None), ("lr", 1e-3), ("b1", 0.9), ("b2", 0.95),
+        ("eps", 1e-8), ("wd", 0.1), ("step", 1), ("st", None))]
+    assert sp(*sargs(n=40)) == UNS
+    assert sp(*sargs(step=0)) == INV
+    assert sp(*sargs(eps=0.0)) == INV
+    assert sp(*sargs(s_w=None)) == INV
+    assert sp(*sargs(m2o=None)) == INV
+    assert sp(*sargs(wo=_vp(ok + base["wo"] + 8))) == INV
+    assert sp(*sargs(missed=_vp(ok + 2))) == INV
+    assert sp(*sargs(m1o=_vp(ok + base["m1"]))) == INV                 # in place
+    assert sp(*sargs(m2o=_vp(ok + base["w"] + 64))) == INV             # overlaps the weights read
+    assert sp(*sargs(wo=_vp(ok + base["m2o"] + 64))) == INV            # overlaps another output
+    assert sp(*sargs(wb=_vp(ok + base["m1o"]))) == INV                 # bf16 weights over m1_out
+    assert sp(*sargs(g8=_vp(ok + base["wo"] + 112))) == INV            # gradient read inside w16_out
     im = lib.fp8_adam_init_master
     assert im(40, _vp(ok), _vp(ok), _vp(ok), None) == UNS
     assert im(64, None, _vp(ok), _vp(ok), None) == INV

@@ -1,5 +1,5 @@
-"""O2 precision-decoupled Adam step (fp8_adam_init_master, fp8_adam_step)
-through the C ABI, against oracle.adam.
+"""O2 precision-decoupled Adam step (fp8_adam_init_master, fp8_adam_step,
+fp8_adam_step_spec) through the C ABI, against oracle.adam.
 
 [FP8-LM reading note, "Proposed method", O2: first moment FP8, second
 moment FP16, master weights FP16 with tensor scaling.] Each step starts
@@ -13,7 +13,10 @@ weights, |beta1 m1| + |(1 - beta1) g| for the first moment: where the
 update nearly cancels w, the fp32 error is relative to the operands, not
 to the small result); the new per-tensor biases must equal the oracle's unless the
 oracle's max lies within 1e-5 (relative) of a power-of-two boundary.
-Master-weight initialisation is bit-exact.
+Master-weight initialisation is bit-exact. The one-pass step
+(fp8_adam_step_spec) must store the two-pass step's state bit for bit,
+records included, both on steps where a scale changes (its second kernel
+recomputes) and on steps where none does, and report which records changed.
 """
 import math
 
@@ -147,3 +150,63 @@ def test_adam_full_size_gpt7b_proj_weight():
     tsf.fp8_adam_step(st, g8, s_g, w_bf16=w_out, **HP)
     torch.cuda.synchronize()
     _check_step(before, st, w_out, g8, s_g, 1)
+
+
+def _rec_fields(r):
+    d = tsf.read_scale(r)
+    return (d["bias"], d["flags"], f32_bits(d["amax"]), d["scale"], d["scale_inv"], d["reduce_bits"])
+
+
+def _same_state(a, b):
+    for x, y in ((a.m1, b.m1), (a.m2, b.m2), (a.w16, b.w16)):
+        assert torch.equal(x, y)
+    for x, y in ((a.s_m1, b.s_m1), (a.s_m2, b.s_m2), (a.s_w, b.s_w)):
+        assert _rec_fields(x) == _rec_fields(y)
+
+
+@pytest.mark.parametrize("n,sigma_w,sigma_g", [(272 * 528, 0.02, 1e-5), (4096 * 16, 0.5, 1e-3)])
+def test_adam_spec_equals_two_pass(n, sigma_w, sigma_g):
+    """Ten steps with one fixed gradient: the moments grow geometrically, so
+    some steps move a tensor's max across a power of two (the second pass
+    runs) and others do not; every step's state, records and bf16 weights
+    equal the two-pass step's, and the reported mask equals the records
+    whose bias changed."""
+    g = np.random.Generator(np.random.PCG64(n + 9))
+    wb = to_dev_bf16(oracle.f64_to_bf16_rne(g.standard_normal(n) * sigma_w))
+    a, b = tsf.AdamState(wb), tsf.AdamState(wb)
+    _same_state(a, b)
+    g8, s_g = _grad(n, n + 10, sigma_g)
+    wa = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    wbo = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    missed = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    masks = []
+    for step in range(1, 11):
+        before = [tsf.read_scale(r)["bias"] for r in (b.s_m1, b.s_m2, b.s_w)]
+        host_before = _state_host(b)
+        tsf.fp8_adam_step(a, g8, s_g, w_bf16=wa, **HP)
+        tsf.fp8_adam_step_spec(b, g8, s_g, w_bf16=wbo, missed=missed, **HP)
+        torch.cuda.synchronize()
+        _same_state(a, b)
+        assert torch.equal(wa.view(torch.int16), wbo.view(torch.int16)), step
+        after = [tsf.read_scale(r)["bias"] for r in (b.s_m1, b.s_m2, b.s_w)]
+        mask = int(missed.item())
+        assert mask == sum(1 << i for i in range(3) if before[i] != after[i]), (step, mask, before, after)
+        masks.append(mask)
+        if step <= 2:
+            _check_step(host_before, b, wbo, g8, s_g, step)
+    assert masks[0] != 0 and 0 in masks, masks      # both paths taken
+
+
+def test_adam_spec_full_size_gpt7b_proj_weight():
+    """A full GPT-7B proj weight (4096 x 4096): two one-pass steps equal two
+    two-pass steps bit for bit."""
+    n = 4096 * 4096
+    g = np.random.Generator(np.random.PCG64(79))
+    wb = to_dev_bf16(oracle.f64_to_bf16_rne(g.standard_normal(n) * 0.02))
+    a, b = tsf.AdamState(wb), tsf.AdamState(wb)
+    for step in (1, 2):
+        g8, s_g = _grad(n, 80 + step, 1e-5)
+        tsf.fp8_adam_step(a, g8, s_g, **HP)
+        tsf.fp8_adam_step_spec(b, g8, s_g, **HP)
+        torch.cuda.synchronize()
+        _same_state(a, b)
