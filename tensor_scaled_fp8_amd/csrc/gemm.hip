@@ -43,7 +43,9 @@
 //    each wave stages its block in LDS a quarter at a time and writes C in
 //    whole 256-byte row pieces (scattered 8-byte stores would leave partial
 //    cache lines and multiply HBM writes); a quarter's stores drain while
-//    the next is converted.
+//    the next is converted. The stores are nontemporal: C is written once
+//    and read by a later kernel, and streaming it out during the GEMM keeps
+//    the write-back of its dirty lines out of the kernels that follow.
 //  * Tiles are numbered so that each XCD (workgroups are dealt round-robin
 //    over the 8 XCDs) works on one contiguous, row-grouped region of C and
 //    its operand panels stay in that XCD's L2.
@@ -654,7 +656,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int tile, fp8_sca
     uint16_t* cp = C + (int64_t)row * N + col;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      if (FULL || (col_ok && row + 4 * k < M)) *(u32x4*)cp = v[k];
+      if (FULL || (col_ok && row + 4 * k < M)) __builtin_nontemporal_store(v[k], (u32x4*)cp);
       cp += (int64_t)4 * N;
     }
   };
@@ -1210,7 +1212,7 @@ __device__ __forceinline__ void gemm_tile16(const GemmParams& p, int tile, fp8_s
     uint16_t* cp = C + (int64_t)row * N + col;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      if (FULL || (col_ok && row + 4 * k < M)) *(u32x4*)cp = v[k];
+      if (FULL || (col_ok && row + 4 * k < M)) __builtin_nontemporal_store(v[k], (u32x4*)cp);
       cp += (int64_t)4 * N;
     }
   };
@@ -1379,7 +1381,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tail_fixup_kernel(GemmParams
       const int r = r0 + 8 * k;  // row within the 64-row region
       const u32x4 v = *(const lds_u32x4*)(src + r * 512 + ((c ^ (r & 31)) << 4));
       const int grow = m0 + 64 * reg + r;
-      if (col_ok && grow < M) *(u32x4*)(p.C + (int64_t)grow * N + n0 + 8 * c) = v;
+      if (col_ok && grow < M) __builtin_nontemporal_store(v, (u32x4*)(p.C + (int64_t)grow * N + n0 + 8 * c));
     }
   }
 }
