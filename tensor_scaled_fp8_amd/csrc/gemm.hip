@@ -869,10 +869,9 @@ __device__ __forceinline__ void gemm_tile16(const GemmParams& p, int tile, fp8_s
   // (r = 0..7), and lane i receives byte i of each of the 8 rows. Group G =
   // l / 16 takes k-rows 32 G + 8 t + r (t = 0..3, one read each), so lane l
   // gets output l % 16 of the block with k = 32 G .. 32 G + 31, the bytes
-  // the row layout hands it. The wave's block m is chunk 8 w + m, stored at
-  // 8 w + (m ^ r) in those rows: toff[m] holds lane's offset for block m,
-  // read t adds 2048 t. The rows of one read differ in k & 7, so they fall
-  // in distinct banks.
+  // the row layout hands it. The wave's block m of B is chunk 8 wn + m,
+  // stored at 8 wn + (m ^ r) in those rows; read t adds 2048 t. The rows of
+  // one read differ in k & 7, so they fall in distinct banks.
   // toff(m) = tbase + ((m ^ r) << 4) = tbase + ((m << 4) ^ trx): two
   // registers, the XOR done per fragment (with trx passed through an empty
   // asm once per stage, so eight precomputed offsets are not held)
